@@ -1,0 +1,93 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4 only).
+//
+// MFMA used throughout: v_mfma_f32_32x32x16_bf16, D[32x32] += A[32x16] * B[16x32].
+// Lane layout (64 lanes, h = lane / 32, n = lane % 32):
+//   A operand: lane holds A[n][8h + e], e = 0..7         (row n, 8 consecutive k)
+//   B operand: lane holds B[8h + e][n], e = 0..7         (column n, 8 consecutive k)
+//   D result : lane holds D[8(r/4) + 4h + (r%4)][n], r = 0..15
+// The k index of one MFMA may be any permutation of the 16 reduction positions as
+// long as A and B agree; the kernels use that to feed a D result straight back in
+// as the next product's B operand.
+//
+// ds_read_b64_tr_b16 (LDS transpose read, 4 x 16-bit per lane): inside every group
+// of 16 lanes, if source lane j supplies the address of 4 consecutive elements
+// x_j[0..3], destination lane i receives x_{4e + i/4}[i % 4] for e = 0..3. Pointing
+// source lane j at row (r0 + j/4), column (c0 + 4 (j%4)) of a row-major tile hands
+// lane i the column c0 + i, rows r0..r0+3: a transposed operand read from a tile
+// stored in its natural [row][d] layout.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Round two floats to bf16 (nearest-even) and pack them, first one in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// 16-byte LDS read (ds_read_b128); `p` must point into a __shared__ array.
+__device__ __forceinline__ bf16x8_t lds_read8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *(const FA_LDS u32x4_t*)(p));
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16) of 4 bf16; see the header comment.
+__device__ __forceinline__ u32x2_t lds_read_tr4(const uint16_t* p) {
+  s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+__device__ __forceinline__ bf16x8_t join8(u32x2_t lo, u32x2_t hi) {
+  u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Exchange with lane (lane ^ 32) and combine: one v_permlane32_swap.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2). Map the
+// hardware id to a logical id so that consecutive logical ids run on one XCD.
+__device__ __forceinline__ int xcd_remap(int hw, int n) {
+  const int x = hw & 7, slot = hw >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return x * per + (x < rem ? x : rem) + slot;
+}
+
+}  // namespace fa

@@ -1,0 +1,167 @@
+// C-ABI entry points of libfa.so (declared and documented in include/fa.h).
+// Every entry point validates its arguments on the host before touching the HIP
+// runtime, then enqueues the kernels of kernels.h on the caller's stream.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_bf16_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_HEADS;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  // Kernels index rows with 32-bit ints and elements with 64-bit offsets.
+  const long long rows_q = (long long)B * Hq * Nq, rows_k = (long long)B * Hkv * Nk;
+  if (rows_q > 0x7fffffffLL || rows_k > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+fa::AttnShape shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal) {
+  fa::AttnShape s;
+  s.B = B; s.Hq = Hq; s.Hkv = Hkv; s.Nq = Nq; s.Nk = Nk; s.d = d;
+  s.scale = scale; s.causal = causal != 0;
+  return s;
+}
+
+constexpr int kMaxSplits = 1024;
+constexpr int kSplitMaxRows = 16;  // (Hq/Hkv) * Nq handled by one split workgroup
+
+size_t splitkv_part_o_bytes(int B, int Hq, int Nq, int d, int splits) {
+  return align256((size_t)B * Hq * Nq * splits * d * sizeof(float));
+}
+size_t splitkv_part_lse_bytes(int B, int Hq, int Nq, int splits) {
+  return align256((size_t)B * Hq * Nq * splits * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is <= 0";
+    case FA_ERR_HEADS: return "FA_ERR_HEADS: Hq is not a multiple of Hkv";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension d not supported by this entry point";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: problem exceeds the library's index range";
+    case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    default: return "unknown fa status code";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+           int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (!supported_bf16_dim(d)) return FA_ERR_HEAD_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  return launch_status(fa::launch_fwd_bf16(
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+      shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), (hipStream_t)stream));
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+               int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (d % 4 != 0 || d > 256) return FA_ERR_HEAD_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  return launch_status(fa::launch_fwd_f32(q, k, v, o, lse,
+                                          shape(B, Hq, Hkv, Nq, Nk, d, scale, causal),
+                                          (hipStream_t)stream));
+}
+
+int fa_splitkv_default_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || Hq % Hkv) return 1;
+  // Aim for about four workgroups per compute unit (256 CUs) with at least 256 keys
+  // per chunk; never more chunks than keys allow.
+  const long long groups = (long long)B * Hkv;
+  long long s = (1024 + groups - 1) / groups;
+  const long long by_len = (Nk + 255) / 256;
+  if (s > by_len) s = by_len;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return (int)s;
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                      int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  const int s = num_splits > 0 ? num_splits
+                               : fa_splitkv_default_splits(B, Hq, Hkv, Nq, Nk, d);
+  return splitkv_part_o_bytes(B, Hq, Nq, d, s) + splitkv_part_lse_bytes(B, Hq, Nq, s);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (!supported_bf16_dim(d)) return FA_ERR_HEAD_DIM;
+  if ((Hq / Hkv) * (long long)Nq > kSplitMaxRows) return FA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
+  const int s = num_splits > 0 ? num_splits : fa_splitkv_default_splits(B, Hq, Hkv, Nq, Nk, d);
+  if (s > Nk) return FA_ERR_SPLITS;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t need = fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, s);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  float* part_o = (float*)workspace;
+  float* part_lse = (float*)((char*)workspace + splitkv_part_o_bytes(B, Hq, Nq, d, s));
+  return launch_status(fa::launch_fwd_splitkv(
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, part_o,
+      part_lse, s, shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), (hipStream_t)stream));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  return align256((size_t)B * Hq * Nq * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (!supported_bf16_dim(d)) return FA_ERR_HEAD_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
+    return FA_ERR_WORKSPACE;
+  return launch_status(fa::launch_bwd(
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+      (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, (float*)workspace,
+      shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), (hipStream_t)stream));
+}
+
+}  // extern "C"

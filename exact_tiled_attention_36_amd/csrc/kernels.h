@@ -1,0 +1,35 @@
+// Internal launch interface between the C-ABI layer (fa_api.hip) and the kernels.
+// Shapes have been validated by the caller; these functions only enqueue work.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AttnShape {
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+};
+
+// Forward, bf16 in/out (d in {64,128,256}).
+hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           uint16_t* o, float* lse, const AttnShape& s, hipStream_t st);
+
+// Forward, fp32 in/out (d % 4 == 0, d <= 256).
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                          float* lse, const AttnShape& s, hipStream_t st);
+
+// Split-KV forward + merge. `part_o` [B,Hq,Nq,splits,d] fp32, `part_lse`
+// [B,Hq,Nq,splits] fp32.
+hipError_t launch_fwd_splitkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint16_t* o, float* lse, float* part_o, float* part_lse,
+                              int splits, const AttnShape& s, hipStream_t st);
+
+// Backward. `dvec` [B,Hq,Nq] fp32 scratch for D_i = rowsum(dO * O).
+hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* o, const uint16_t* dO, const float* lse,
+                      uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec,
+                      const AttnShape& s, hipStream_t st);
+
+}  // namespace fa

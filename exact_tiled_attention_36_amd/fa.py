@@ -1,0 +1,181 @@
+"""Python binding of libfa.so (ctypes). Argument marshalling only.
+
+PyTorch supplies device memory and streams; every step of the attention computation
+runs in the library's HIP kernels. There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+
+The library must share PyTorch's HIP runtime. Both carry the soname
+``libamdhip64.so.7``; importing torch first makes the loader resolve libfa.so's
+dependency to the runtime torch already loaded, so device pointers and stream handles
+are valid on both sides.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+_lib = None
+
+_c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes)
+_SIGNATURES = {
+    "fa_version": (_c_int, []),
+    "fa_status_string": (ctypes.c_char_p, [_c_int]),
+    "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "fa_fwd_f32": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "fa_splitkv_default_splits": (_c_int, [_c_int] * 6),
+    "fa_fwd_splitkv_workspace_bytes": (_c_size, [_c_int] * 7),
+    "fa_fwd_splitkv": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6
+                       + [_c_float, _c_int, _c_int, _vp, _c_size, _vp]),
+    "fa_bwd_workspace_bytes": (_c_size, [_c_int] * 6),
+    "fa_bwd": (_c_int, [_vp] * 10 + [_c_size] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load(path: Optional[str] = None, require_torch: bool = True):
+    """Load libfa.so once and attach the C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    if require_torch:
+        import torch  # noqa: F401  (loads the HIP runtime the library must share)
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run __graft_entry__.build() or "
+                           "python -m exact_tiled_attention_36_amd.build")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FAError(fn, status, status_string(status))
+
+
+def _stream(dev) -> int:
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dims(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
+        out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O and LSE for bf16 (fa_fwd) or float32 (fa_fwd_f32) inputs."""
+    import torch
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.bfloat16:
+        fn, name = lib.fa_fwd, "fa_fwd"
+    elif q.dtype == torch.float32:
+        fn, name = lib.fa_fwd_f32, "fa_fwd_f32"
+    else:
+        raise ValueError("dtype must be bfloat16 or float32")
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)), _stream(q.device))
+    _check(name, st)
+    return out, lse
+
+
+def splitkv_default_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return load().fa_splitkv_default_splits(B, Hq, Hkv, Nq, Nk, d)
+
+
+def splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits=0) -> int:
+    return load().fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
+
+
+def fwd_splitkv(q, k, v, causal: bool = True, scale: Optional[float] = None,
+                num_splits: int = 0, out=None, lse=None, workspace=None):
+    """Split-KV forward (decode shapes), bf16."""
+    import torch
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("fa_fwd_splitkv takes bfloat16")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    nbytes = lib.fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)),
+                            int(num_splits), workspace.data_ptr(), workspace.numel(),
+                            _stream(q.device))
+    _check("fa_fwd_splitkv", st)
+    return out, lse
+
+
+def bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return load().fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+
+
+def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV (bf16) by recomputation from the forward's O and LSE."""
+    import torch
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("o", o), ("do", do)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q")
+    if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Nq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nbytes = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, Nq, Nk, d, sc,
+                    int(bool(causal)), _stream(q.device))
+    _check("fa_bwd", st)
+    return dq, dk, dv

@@ -1,0 +1,129 @@
+/*
+ * fa.h — C ABI of the exact tiled attention library (libfa.so), MI355X / gfx950.
+ *
+ * What is computed. For every batch b and query head h, with key/value head
+ * kvh = h / (Hq / Hkv):
+ *     s_ij = scale * q_i . k_j              (scores; the pages' value of scale is 1/sqrt(d))
+ *     p_ij = exp(s_ij - lse_i)              (row softmax of the visible scores)
+ *     lse_i = log(sum_j exp(s_ij))          (natural log, of the scaled scores)
+ *     o_i   = sum_j p_ij v_j
+ * ("FlashAttention" (ruizhehou.github.io), §一: scores Q K^T / sqrt(d), softmax,
+ * times V; FlashAttention1 article (gitcode.csdn.net), §一: the same formula.)
+ * The forward pass forms the scores tile by tile with online softmax — running row
+ * max m and row sum l, rescale by exp(m_old - m_new), one division at the end — so
+ * no N x N matrix is ever written to memory ("FlashAttention" (ruizhehou.github.io),
+ * §二.1 tiling, §二.2 online softmax, §四.1 deferred normalisation). It keeps one
+ * float per row, lse = m + ln(l), for the backward pass, which rebuilds P from it
+ * (§二.3 recomputation).
+ *
+ * Causal masking (causal != 0) is aligned to the bottom-right corner: query row i
+ * sees key j iff j <= i + (Nk - Nq). With Nq == Nk this is the lower triangle; with
+ * Nq == 1 (decode) the row sees every key. A row that sees no key (only possible
+ * when Nq > Nk) gets o = 0 and lse = -inf. Grouped/multi-query attention
+ * ("FlashAttention" (newton.com.tw wiki), 發展歷程, FlashAttention-2 paragraph):
+ * Hq must be a multiple of Hkv; query head h uses key/value head h / (Hq / Hkv).
+ *
+ * Layouts. All tensors are dense and row-major with the head dimension fastest:
+ *     q, o, dO, dq : [B, Hq,  Nq, d]
+ *     k, v, dk, dv : [B, Hkv, Nk, d]
+ *     lse          : [B, Hq,  Nq]   float32
+ * bf16 entry points take IEEE bfloat16 bit patterns (2 bytes per element);
+ * fa_fwd_f32 takes float32. Every tensor pointer must be 16-byte aligned.
+ *
+ * Ownership and errors. Pointers are device pointers owned by the caller; the
+ * library keeps no pointer after a call returns and allocates nothing. Outputs are
+ * fully overwritten (no zeroing needed). Calls are asynchronous: work is enqueued
+ * on `stream` (a hipStream_t; NULL means the default stream) and the library never
+ * synchronises. Arguments are validated before any HIP call; on a bad argument the
+ * call returns a negative FA_ERR_* code and enqueues nothing. FA_ERR_LAUNCH means a
+ * kernel launch was rejected by the runtime. fa_status_string() names every code.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,       /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = -2,      /* a size is <= 0 (Nk may not be 0 either)             */
+  FA_ERR_HEADS = -3,      /* Hq is not a multiple of Hkv                         */
+  FA_ERR_HEAD_DIM = -4,   /* d not supported by this entry point                 */
+  FA_ERR_ALIGN = -5,      /* a tensor pointer is not 16-byte aligned             */
+  FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than the size asked for   */
+  FA_ERR_LAUNCH = -7,     /* the HIP runtime rejected a kernel launch            */
+  FA_ERR_TOO_LARGE = -8,  /* an index would overflow 32/64-bit addressing limits */
+  FA_ERR_SPLITS = -9,     /* num_splits out of range                             */
+  FA_ERR_SCALE = -10      /* scale is not a finite number > 0                    */
+};
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Forward pass, bfloat16 inputs and output, float32 accumulation.
+ * Writes o (bf16) and lse (float32). d must be 64, 128 or 256.
+ * Work is gridded over (batch, head, block of query rows): the sequence-dimension
+ * parallelism of "FlashAttention" (ruizhehou.github.io), §四.2. Causal calls skip
+ * key tiles that lie wholly above the diagonal.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+           void* stream);
+
+/*
+ * Forward pass, float32 inputs and output, float32 arithmetic throughout.
+ * Same contract as fa_fwd; d must be a multiple of 4 in [4, 256].
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+               void* stream);
+
+/*
+ * Split-KV forward for short query blocks (decode). Same result and layouts as
+ * fa_fwd, but the keys of every (batch, kv-head) are cut into num_splits chunks that
+ * run in separate workgroups; each chunk leaves a normalised partial output and its
+ * log-sum-exp in `workspace`, and a second kernel merges the chunks by the online-
+ * softmax rescale rule ("FlashAttention" (ruizhehou.github.io), §二.2, applied to
+ * whole chunks). This fills the GPU when B * Hq * Nq is small and Nk is long.
+ * Requires (Hq / Hkv) * Nq <= 16 and d in {64, 128, 256}. num_splits in
+ * [1, 1024]; pass 0 to let the library choose (fa_splitkv_default_splits).
+ * workspace must hold fa_fwd_splitkv_workspace_bytes(...) bytes (16-byte aligned,
+ * contents ignored on entry).
+ */
+int fa_splitkv_default_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                      int num_splits);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                   int causal, int num_splits, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Backward pass by recomputation ("FlashAttention" (ruizhehou.github.io), §二.3):
+ * from q, k, v, the forward's o and lse, and the upstream gradient dO, rebuild each
+ * block of P = exp(s - lse) and write dq, dk, dv (bf16, same layouts as q, k, v).
+ * The chain rule used (the pages give no backward formulas): D_i = sum_c dO_ic o_ic,
+ * dP = dO V^T, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
+ * with dK and dV summed over the query heads that share a kv-head.
+ * workspace must hold fa_bwd_workspace_bytes(...) bytes (16-byte aligned; contents
+ * ignored on entry). d must be 64, 128 or 256.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+           float scale, int causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,73 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, compare with
+the oracle, and print the case name before each GPU step."""
+import sys
+
+import numpy as np
+
+from exact_tiled_attention_36_amd import synth
+
+# Tolerances (from the method's accuracy targets): bf16 O max abs 2e-2 and mean abs
+# 2e-3; gradients max abs error / max abs oracle value 5e-2 per tensor; fp32 O max
+# abs 1e-4. LSE tolerances are this build's: bf16 1e-3 (scores are exact fp32 dot
+# products of bf16 inputs, the row sum is fp32), fp32 1e-5.
+TOL_O_MAX = 2e-2
+TOL_O_MEAN = 2e-3
+TOL_GRAD_REL = 5e-2
+TOL_F32_O = 1e-4
+TOL_LSE_BF16 = 1e-3
+TOL_LSE_F32 = 1e-5
+
+
+def announce(msg: str):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(inp: synth.AttnInputs, name: str):
+    import torch
+    a = getattr(inp, name)
+    if inp.dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to("cuda")
+
+
+def to_host64(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        bits = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+        return synth.bf16_bits_to_f64(bits)
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def err_stats(got: np.ndarray, ref: np.ndarray):
+    diff = np.abs(got - ref)
+    finite = np.isfinite(ref)
+    if not np.all(finite == np.isfinite(got)):
+        return float("inf"), float("inf")
+    dd = np.where(finite, diff, 0.0)
+    same_inf = np.where(finite, True, got == ref)
+    if not np.all(same_inf):
+        return float("inf"), float("inf")
+    return float(dd.max(initial=0.0)), float(dd.mean()) if dd.size else 0.0
+
+
+def assert_o_close(got, ref, what=""):
+    mx, mean = err_stats(got, ref)
+    assert mx <= TOL_O_MAX and mean <= TOL_O_MEAN, f"{what}: O max {mx:.3e} mean {mean:.3e}"
+    return mx, mean
+
+
+def assert_lse_close(got, ref, tol, what=""):
+    mx, _ = err_stats(got, ref)
+    assert mx <= tol, f"{what}: LSE max {mx:.3e}"
+    return mx
+
+
+def assert_grad_close(got, ref, what=""):
+    scale = float(np.abs(ref).max())
+    mx = float(np.abs(got - ref).max())
+    rel = mx / scale if scale > 0 else mx
+    assert rel <= TOL_GRAD_REL, f"{what}: max abs err {mx:.3e} / max |ref| {scale:.3e} = {rel:.3e}"
+    return rel
