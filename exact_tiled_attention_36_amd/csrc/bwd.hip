@@ -1,0 +1,487 @@
+// Backward attention by recomputation, bf16 in/out, fp32 accumulation, for gfx950.
+//
+// The forward pass keeps only the per-row statistics; the backward pass rebuilds
+// every block of P from them instead of reading a stored N x N matrix
+// ("FlashAttention" (ruizhehou.github.io), §二.3 recomputation; the statistics m and
+// l are folded into lse = m + ln l, so P = exp(s - lse)). The pages give no formulas
+// for the gradients; these kernels use the chain rule of softmax attention:
+//     D_i  = sum_c dO_ic O_ic        (equals sum_j P_ij dP_ij)
+//     dP   = dO V^T,  dS = P * (dP - D)
+//     dV   = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K
+// with dK, dV summed over the query heads that share a key/value head.
+//
+// Three kernels on one stream:
+//  1. bwd_pre:  D for every query row (HBM-bound row dot products).
+//  2. bwd_dkdv: one workgroup per (batch, kv-head, 128 keys); each wave keeps 32 keys
+//     of K and V in registers and loops over the group's query heads and the query
+//     blocks that can see its keys, with Q/dO/LSE/D tiles double buffered in LDS.
+//     S = Q K^T and dP = dO V^T come out with one key per lane, so P and dS (rounded
+//     to bf16) feed dV^T += dO^T P and dK^T += Q^T dS directly as B operands; dO^T
+//     and Q^T are read with LDS transpose loads.
+//  3. bwd_dq:   one workgroup per (batch, head, 128 queries); Q and dO stay in
+//     registers, K/V tiles are double buffered in LDS; S^T and dP^T put one query per
+//     lane, so LSE and D are per-lane scalars, and dQ^T += K^T dS^T reads K^T with
+//     LDS transpose loads.
+// No atomics: every output element is written by exactly one workgroup, so results
+// are bitwise reproducible.
+#include "common.h"
+#include "kernels.h"
+
+namespace fa {
+namespace {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dO;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dvec;
+  int Hq, Hkv, Nq, Nk, g, causal_off;
+  float scale, scale_log2;
+};
+
+// ---------------------------------------------------------------------------------
+// 1. D_i = sum_c dO_ic * O_ic
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int rows) {
+  constexpr int LPR = D / 8;        // lanes per row, 8 elements (16 bytes) each
+  constexpr int RPB = 256 / LPR;    // rows per workgroup pass
+  const int tid = threadIdx.x, sub = tid % LPR;
+  for (int row = blockIdx.x * RPB + tid / LPR; row < rows; row += gridDim.x * RPB) {
+    const u32x4_t a = ((const u32x4_t*)(p.o + (size_t)row * D))[sub];
+    const u32x4_t b = ((const u32x4_t*)(p.dO + (size_t)row * D))[sub];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
+      acc = fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
+    }
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
+    if (sub == 0) p.dvec[row] = acc;
+  }
+}
+
+// Row statistic as used by the recompute: log2-domain LSE, +inf for rows that must
+// contribute nothing (padding rows past Nq, and rows that saw no key at all).
+__device__ __forceinline__ float lse2_of(const BwdParams& p, size_t idx, bool valid) {
+  if (!valid) return INFINITY;
+  const float l = p.lse[idx];
+  return l == -INFINITY ? INFINITY : l * kLog2e;
+}
+
+// ---------------------------------------------------------------------------------
+// 2. dK, dV
+// ---------------------------------------------------------------------------------
+template <int D, int BMQ>
+struct DkdvTile {
+  static constexpr int STR = D + 8;
+  static constexpr int TILE = BMQ * STR;
+  static constexpr int LPT = BMQ * D / 8 / 256;
+  static_assert(LPT * 256 * 8 == BMQ * D, "tile must split evenly");
+};
+
+template <int D, int BMQ, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) {
+  using T = DkdvTile<D, BMQ>;
+  constexpr int STR = T::STR, LPT = T::LPT, CPR = D / 8;
+  constexpr int NDC = D / 16, NCB = D / 32, NQS = BMQ / 32;
+  constexpr int BNK = 128;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * T::TILE];
+  __shared__ __attribute__((aligned(16))) float svec[2 * 2 * BMQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = L % nkb, bkv = L / nkb;
+  const int kvh = bkv % p.Hkv, b = bkv / p.Hkv;
+  const int k0 = kb * BNK;
+  const int key = k0 + 32 * w + l32;
+
+  bf16x8_t kreg[NDC], vreg[NDC];
+  {
+    const size_t base = ((size_t)(b * p.Hkv + kvh) * p.Nk + (key < p.Nk ? key : p.Nk - 1)) * D;
+    const u32x4_t* ks = (const u32x4_t*)(p.k + base + 8 * hi);
+    const u32x4_t* vs = (const u32x4_t*)(p.v + base + 8 * hi);
+    const u32x4_t z = {0, 0, 0, 0};
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      kreg[dc] = __builtin_bit_cast(bf16x8_t, key < p.Nk ? ks[2 * dc] : z);
+      vreg[dc] = __builtin_bit_cast(bf16x8_t, key < p.Nk ? vs[2 * dc] : z);
+    }
+  }
+
+  int i_start = 0;
+  if (CAUSAL) {
+    i_start = k0 - p.causal_off;
+    if (i_start < 0) i_start = 0;
+  }
+  const int nqb = (p.Nq + BMQ - 1) / BMQ;
+  const int qb0 = i_start / BMQ;
+  const int per_head = nqb - qb0 > 0 ? nqb - qb0 : 0;
+  const int total = per_head * p.g;
+
+  f32x16_t dkacc[NCB], dvacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    dkacc[cb] = zero16();
+    dvacc[cb] = zero16();
+  }
+  const float c2 = p.scale_log2;
+
+  u32x4_t qpre[LPT], dopre[LPT];
+  float lpre = 0.f, dpre = 0.f;
+  auto gload = [&](int s) {
+    const int h = kvh * p.g + s / per_head;
+    const int i0 = (qb0 + s % per_head) * BMQ;
+    const size_t hbase = (size_t)(b * p.Hq + h) * p.Nq;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
+      const int qi = i0 + row;
+      if (qi < p.Nq) {
+        qpre[i] = ((const u32x4_t*)(p.q + (hbase + qi) * D))[col];
+        dopre[i] = ((const u32x4_t*)(p.dO + (hbase + qi) * D))[col];
+      } else {
+        qpre[i] = u32x4_t{0, 0, 0, 0};
+        dopre[i] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+    if (tid < BMQ) {
+      const int qi = i0 + tid;
+      lpre = lse2_of(p, hbase + qi, qi < p.Nq);
+      dpre = qi < p.Nq ? p.dvec[hbase + qi] : 0.f;
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* Qs = smem + buf * 2 * T::TILE;
+    uint16_t* Os = Qs + T::TILE;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
+      *(FA_LDS u32x4_t*)(Qs + row * STR + col * 8) = qpre[i];
+      *(FA_LDS u32x4_t*)(Os + row * STR + col * 8) = dopre[i];
+    }
+    if (tid < BMQ) {
+      svec[buf * 2 * BMQ + tid] = lpre;
+      svec[buf * 2 * BMQ + BMQ + tid] = dpre;
+    }
+  };
+
+  if (total > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int wkey0 = k0 + 32 * w;  // first key of this wave
+
+  for (int s = 0; s < total; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < total) gload(s + 1);
+    const uint16_t* Qs = smem + buf * 2 * T::TILE;
+    const uint16_t* Os = Qs + T::TILE;
+    const float* Ls = svec + buf * 2 * BMQ;
+    const float* Ds = Ls + BMQ;
+    const int i0 = (qb0 + s % per_head) * BMQ;
+
+#pragma unroll
+    for (int qs = 0; qs < NQS; ++qs) {
+      const int ib = i0 + 32 * qs;
+      // every (query, key) pair of this wave's 32x32 block is above the diagonal
+      if (CAUSAL && ib + 31 + p.causal_off < wkey0) continue;
+      f32x16_t S = zero16(), dP = zero16();
+      const uint16_t* qp = Qs + (32 * qs + l32) * STR + 8 * hi;
+      const uint16_t* op = Os + (32 * qs + l32) * STR + 8 * hi;
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        S = mfma32x32x16(lds_read8(qp + 16 * dc), kreg[dc], S);
+        dP = mfma32x32x16(lds_read8(op + 16 * dc), vreg[dc], dP);
+      }
+      const bool need_mask = CAUSAL && (ib + p.causal_off < wkey0 + 31);
+      uint32_t ppk[8], dspk[8];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4_t l4 = *(const FA_LDS f32x4_t*)(Ls + 32 * qs + 8 * rg + 4 * hi);
+        const f32x4_t d4 = *(const FA_LDS f32x4_t*)(Ds + 32 * qs + 8 * rg + 4 * hi);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          float pr = fast_exp2(fmaf(S[r], c2, -l4[e]));
+          if (need_mask && key > ib + 8 * rg + 4 * hi + e + p.causal_off) pr = 0.f;
+          pv[e] = pr;
+          dsv[e] = pr * (dP[r] - d4[e]);
+        }
+        ppk[2 * rg] = pack_bf16x2(pv[0], pv[1]);
+        ppk[2 * rg + 1] = pack_bf16x2(pv[2], pv[3]);
+        dspk[2 * rg] = pack_bf16x2(dsv[0], dsv[1]);
+        dspk[2 * rg + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4_t pu = {ppk[4 * kk], ppk[4 * kk + 1], ppk[4 * kk + 2], ppk[4 * kk + 3]};
+        const u32x4_t du = {dspk[4 * kk], dspk[4 * kk + 1], dspk[4 * kk + 2], dspk[4 * kk + 3]};
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pu);
+        const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
+        const int rowb = 32 * qs + 16 * kk + tr_row;
+        const uint16_t* otr = Os + rowb * STR + tr_col;
+        const uint16_t* qtr = Qs + rowb * STR + tr_col;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const bf16x8_t ao = join8(lds_read_tr4(otr + 32 * cb), lds_read_tr4(otr + 8 * STR + 32 * cb));
+          dvacc[cb] = mfma32x32x16(ao, pb, dvacc[cb]);
+          const bf16x8_t aq = join8(lds_read_tr4(qtr + 32 * cb), lds_read_tr4(qtr + 8 * STR + 32 * cb));
+          dkacc[cb] = mfma32x32x16(aq, db, dkacc[cb]);
+        }
+      }
+    }
+    if (s + 1 < total) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key < p.Nk) {
+    const size_t base = ((size_t)(b * p.Hkv + kvh) * p.Nk + key) * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = 32 * cb + 8 * rg + 4 * hi;
+        const u32x2_t kv = {pack_bf16x2(dkacc[cb][4 * rg] * p.scale, dkacc[cb][4 * rg + 1] * p.scale),
+                            pack_bf16x2(dkacc[cb][4 * rg + 2] * p.scale, dkacc[cb][4 * rg + 3] * p.scale)};
+        const u32x2_t vv = {pack_bf16x2(dvacc[cb][4 * rg], dvacc[cb][4 * rg + 1]),
+                            pack_bf16x2(dvacc[cb][4 * rg + 2], dvacc[cb][4 * rg + 3])};
+        *(u32x2_t*)(p.dk + base + c0) = kv;
+        *(u32x2_t*)(p.dv + base + c0) = vv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// 3. dQ
+// ---------------------------------------------------------------------------------
+template <int D, int BN>
+struct DqTile {
+  static constexpr int STR = D + 8;
+  static constexpr int TILE = BN * STR;
+  static constexpr int LPT = BN * D / 8 / 256;
+  static_assert(LPT * 256 * 8 == BN * D, "tile must split evenly");
+};
+
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
+  using T = DqTile<D, BN>;
+  constexpr int STR = T::STR, LPT = T::LPT, CPR = D / 8;
+  constexpr int NDC = D / 16, NCB = D / 32, NKB = BN / 32;
+  constexpr int BM = 128;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * T::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int qb = L % nqb;
+  const int bh = L / nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int h = bh % p.Hq, b = bh / p.Hq, kvh = h / p.g;
+  const int q0 = qb * BM;
+  const int qrow = q0 + 32 * w + l32;
+  const bool qvalid = qrow < p.Nq;
+  const size_t rowidx = (size_t)(b * p.Hq + h) * p.Nq + (qvalid ? qrow : p.Nq - 1);
+
+  bf16x8_t qreg[NDC], doreg[NDC];
+  {
+    const u32x4_t* qs = (const u32x4_t*)(p.q + rowidx * D + 8 * hi);
+    const u32x4_t* os = (const u32x4_t*)(p.dO + rowidx * D + 8 * hi);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      qreg[dc] = __builtin_bit_cast(bf16x8_t, qs[2 * dc]);
+      doreg[dc] = __builtin_bit_cast(bf16x8_t, os[2 * dc]);
+    }
+  }
+  const float lse2 = lse2_of(p, rowidx, qvalid);
+  const float Dv = qvalid ? p.dvec[rowidx] : 0.f;
+
+  const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+  const uint16_t* Vg = p.v + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+  int kend = p.Nk;
+  if (CAUSAL) {
+    const int lim = q0 + BM + p.causal_off;
+    kend = lim < kend ? lim : kend;
+  }
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  f32x16_t dqacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dqacc[cb] = zero16();
+  const float c2 = p.scale_log2;
+
+  u32x4_t kpre[LPT], vpre[LPT];
+  auto gload = [&](int t) {
+    const int j0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
+      const int j = j0 + row;
+      if (j < p.Nk) {
+        kpre[i] = ((const u32x4_t*)(Kg + (size_t)j * D))[col];
+        vpre[i] = ((const u32x4_t*)(Vg + (size_t)j * D))[col];
+      } else {
+        kpre[i] = u32x4_t{0, 0, 0, 0};
+        vpre[i] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* Ks = smem + buf * 2 * T::TILE;
+    uint16_t* Vs = Ks + T::TILE;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
+      *(FA_LDS u32x4_t*)(Ks + row * STR + col * 8) = kpre[i];
+      *(FA_LDS u32x4_t*)(Vs + row * STR + col * 8) = vpre[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int wq_last = q0 + 32 * w + 31;  // last query of this wave
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const uint16_t* Ks = smem + buf * 2 * T::TILE;
+    const uint16_t* Vs = Ks + T::TILE;
+    const int j0 = t * BN;
+    // skip tiles that lie wholly above this wave's part of the diagonal
+    if (!CAUSAL || j0 <= wq_last + p.causal_off) {
+      f32x16_t S[NKB], dP[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        S[kb] = zero16();
+        dP[kb] = zero16();
+        const uint16_t* kp = Ks + (32 * kb + l32) * STR + 8 * hi;
+        const uint16_t* vp = Vs + (32 * kb + l32) * STR + 8 * hi;
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+          S[kb] = mfma32x32x16(lds_read8(kp + 16 * dc), qreg[dc], S[kb]);
+          dP[kb] = mfma32x32x16(lds_read8(vp + 16 * dc), doreg[dc], dP[kb]);
+        }
+      }
+      const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && (j0 + BN - 1 > q0 + 32 * w + p.causal_off));
+      const int lim = CAUSAL ? qrow + p.causal_off : 0x7fffffff;
+      uint32_t dspk[NKB][8];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float pr = fast_exp2(fmaf(S[kb][r + e], c2, -lse2));
+            if (need_mask) {
+              const int j = j0 + 32 * kb + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
+              if (j >= p.Nk || j > lim) pr = 0.f;
+            }
+            ds2[e] = pr * (dP[kb][r + e] - Dv);
+          }
+          dspk[kb][r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+        }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4_t du = {dspk[kb][4 * kk], dspk[kb][4 * kk + 1], dspk[kb][4 * kk + 2], dspk[kb][4 * kk + 3]};
+          const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
+          const uint16_t* ktr = Ks + (32 * kb + 16 * kk + tr_row) * STR + tr_col;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const bf16x8_t a = join8(lds_read_tr4(ktr + 32 * cb), lds_read_tr4(ktr + 8 * STR + 32 * cb));
+            dqacc[cb] = mfma32x32x16(a, db, dqacc[cb]);
+          }
+        }
+    }
+    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qvalid) {
+    uint16_t* orow = p.dq + rowidx * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = 32 * cb + 8 * rg + 4 * hi;
+        const u32x2_t val = {pack_bf16x2(dqacc[cb][4 * rg] * p.scale, dqacc[cb][4 * rg + 1] * p.scale),
+                             pack_bf16x2(dqacc[cb][4 * rg + 2] * p.scale, dqacc[cb][4 * rg + 3] * p.scale)};
+        *(u32x2_t*)(orow + c0) = val;
+      }
+  }
+}
+
+template <int D, int BMQ, int BN, bool CAUSAL>
+hipError_t run(const BwdParams& p, int B, hipStream_t st) {
+  const int rows = B * p.Hq * p.Nq;
+  {
+    constexpr int RPB = 256 / (D / 8);
+    int nb = (rows + RPB - 1) / RPB;
+    if (nb > 65536) nb = 65536;
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(nb), dim3(256), 0, st, p, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nkb = (p.Nk + 127) / 128;
+    const long long n = (long long)nkb * p.Hkv * B;
+    if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BMQ, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nkb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nqb = (p.Nq + 127) / 128;
+    const long long n = (long long)nqb * p.Hq * B;
+    if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nqb);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* o, const uint16_t* dO, const float* lse,
+                      uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec,
+                      const AttnShape& s, hipStream_t st) {
+  BwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dvec = dvec;
+  p.Hq = s.Hq; p.Hkv = s.Hkv; p.Nq = s.Nq; p.Nk = s.Nk; p.g = s.Hq / s.Hkv;
+  p.causal_off = s.Nk - s.Nq;
+  p.scale = s.scale;
+  p.scale_log2 = s.scale * kLog2e;
+  const bool c = s.causal != 0;
+  switch (s.d) {
+    case 64: return c ? run<64, 64, 64, true>(p, s.B, st) : run<64, 64, 64, false>(p, s.B, st);
+    case 128: return c ? run<128, 64, 64, true>(p, s.B, st) : run<128, 64, 64, false>(p, s.B, st);
+    case 256: return c ? run<256, 32, 32, true>(p, s.B, st) : run<256, 32, 32, false>(p, s.B, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa
