@@ -1,0 +1,291 @@
+"""Throughput of the exact tiled attention path on one MI355X.
+
+One step = the whole hot path on one batch of the GQA training workload
+(B=2, Hq=32, Hkv=8, N=8192, d=128, causal, bf16): forward (fa_fwd) then the
+recompute backward (fa_bwd_stage 0, 1, 2 = D preprocess, dK/dV, dQ), with inputs
+resident in HBM. FLOPs per step follow the method's accounting: 4*B*Hq*Nq*Nk*d for
+the forward, 2.5x that for the backward, halved for causal.
+
+Prints one JSON line. Besides the headline value it carries:
+  roofline      the dominant kernel's algorithmic FLOP/s (HIP events on the launch
+                stream) against the bf16 dense MFMA peak, plus its HBM traffic when a
+                counter summary for the current kernel source is in profiles/;
+  cpu_baseline  the float64 oracle on this host, timed on a bounded sample;
+  phases        per-kernel average milliseconds;
+  extra         forward/decode throughput of the other workloads (fewer iterations).
+
+Modes: default; --profile (no oracle/extras, a known-size copy first, for rocprofv3
+counter runs that calibrate FETCH_SIZE/WRITE_SIZE).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s at 1 GPU and % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "c5_bf16_causal_gqa_B2Hq32Hkv8N8192d128"
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ["fwd_bf16.hip", "common.h"],
+    "bwd_pre_kernel": ["bwd.hip", "common.h"],
+    "bwd_dkdv_kernel": ["bwd.hip", "common.h"],
+    "bwd_dq_kernel": ["bwd.hip", "common.h"],
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, Hq, Nq, Nk, d, causal):
+    f = 4.0 * B * Hq * Nq * Nk * d
+    return f / 2 if (causal and Nq == Nk) else f
+
+
+def source_sha(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_tiled_attention_36_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """Counter-derived HBM bytes per launch from profiles/counters_*.txt, or None when
+    no summary matches the current kernel source."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    want = source_sha(kernel)
+    for fn in sorted(os.listdir(pdir)):
+        if not fn.startswith("counters_") or not fn.endswith(".txt"):
+            continue
+        for line in open(os.path.join(pdir, fn)):
+            if not line.startswith("TRAFFIC "):
+                continue
+            kv = dict(re.findall(r"(\w+)=(\S+)", line))
+            if kv.get("kernel") == kernel and kv.get("workload") == workload \
+                    and kv.get("source_sha") == want:
+                return float(kv["hbm_bytes_per_launch"])
+    return None
+
+
+class Timer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.pairs = {}
+
+    def mark(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        fn()
+        b.record(self.stream)
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def avg_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.pairs.items()}
+
+
+def cpu_baseline(inp, min_seconds=10.0):
+    """The float64 oracle, as written, on a bounded sample of the workload: whole
+    (batch 0, kv-head) groups -- every query head of the group, forward and backward
+    over the full sequence -- added one group at a time until at least `min_seconds`
+    of CPU work. Reported in the same FLOP accounting as the GPU value."""
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    g = inp.Hq // inp.Hkv
+    qa, ka, va, da = (inp.as_f64(n) for n in ("q", "k", "v", "do"))
+    dt, groups = 0.0, 0
+    while dt < min_seconds and groups < inp.Hkv:
+        hs = slice(groups * g, (groups + 1) * g)
+        q, do = qa[:1, hs], da[:1, hs]
+        k, v = ka[:1, groups:groups + 1], va[:1, groups:groups + 1]
+        t0 = time.perf_counter()
+        A.forward(q, k, v, inp.scale, inp.causal)
+        A.backward(q, k, v, do, inp.scale, inp.causal)
+        dt += time.perf_counter() - t0
+        groups += 1
+    fl = 3.5 * fwd_flops(1, groups * g, inp.Nq, inp.Nk, inp.d, inp.causal)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads or cores,
+            "host_cpus": cores, "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"batch 0, {groups} kv-head group(s) = {groups * g} query heads of "
+                      f"{WORKLOAD}: float64 forward + backward over all {inp.Nq} rows, "
+                      "S and P materialised"}
+
+
+def extras(torch, fa, iters=10):
+    """Forward throughput on the other workloads, decode in GB/s (seeded torch.randn)."""
+    from exact_tiled_attention_36_amd import synth
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    for name in ("c2_bf16_B2H16N1024d64", "c3a_bf16_causal_B4H32N4096d128",
+                 "c3b_bf16_causal_B2H16N4096d256", "c4a_bf16_causal_B1H8N32768d128",
+                 "c4b_bf16_decode_B8H8Nq1Nk32768d128"):
+        w = synth.WORKLOADS[name]
+        B, Hq, Hkv, Nq, Nk, d, causal = (w[x] for x in ("B", "Hq", "Hkv", "Nq", "Nk", "d", "causal"))
+        q = torch.randn(B, Hq, Nq, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        k = torch.randn(B, Hkv, Nk, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        v = torch.randn(B, Hkv, Nk, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        decode = Nq == 1
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, Nq, device="cuda", dtype=torch.float32)
+        if decode:
+            ws = torch.empty(fa.splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d), device="cuda",
+                             dtype=torch.uint8)
+            call = lambda: fa.fwd_splitkv(q, k, v, causal=causal, out=o, lse=lse, workspace=ws)
+        else:
+            call = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        for _ in range(3):
+            call()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(iters):
+            call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
+        rec = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+               "pct_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2)}
+        if decode:
+            nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
+            rec["gbs"] = round(nbytes / ms / 1e6, 1)
+            rec["pct_hbm_peak"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS * 100, 2)
+            rec["kernel"] = "fa_fwd_splitkv (chunk + merge)"
+        out[name] = rec
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="counter-run mode: 1 GiB copy first, no oracle, no extras")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the method's heads and batch shard with no communication; see the "
+              "design notes for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from exact_tiled_attention_36_amd import fa, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    if args.profile:
+        a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.add(a, 1.0, out=b)  # elementwise kernel: exactly 1 GiB read, 1 GiB written
+        torch.cuda.synchronize()
+        del a, b
+
+    log(f"generating {WORKLOAD}")
+    inp = synth.workload(WORKLOAD)
+    B, Hq, Hkv, Nq, Nk, d, causal = inp.B, inp.Hq, inp.Hkv, inp.Nq, inp.Nk, inp.d, inp.causal
+
+    def to_dev(name):
+        return torch.from_numpy(getattr(inp, name).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = to_dev("q"), to_dev("k"), to_dev("v"), to_dev("do")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, Nq, device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d), device=dev, dtype=torch.uint8)
+
+    timer = Timer(torch, stream)
+
+    def step(record):
+        run = timer.mark if record else (lambda name, fn: fn())
+        run("fwd_bf16_kernel", lambda: fa.fwd(q, k, v, causal=causal, scale=inp.scale,
+                                              out=o, lse=lse))
+        for stg, name in ((0, "bwd_pre_kernel"), (1, "bwd_dkdv_kernel"), (2, "bwd_dq_kernel")):
+            run(name, lambda stg=stg: fa.bwd(q, k, v, o, do, lse, causal=causal,
+                                             scale=inp.scale, dq=dq, dk=dk, dv=dv,
+                                             workspace=ws, stage=stg))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    f_fwd = fwd_flops(B, Hq, Nq, Nk, d, causal)
+    f_step = 3.5 * f_fwd
+    value = args.steps * f_step / elapsed / 1e12
+    ms = timer.avg_ms()
+
+    # algorithmic flops per launch: dense products each kernel performs (causal halved)
+    per_kernel_flops = {"fwd_bf16_kernel": f_fwd, "bwd_dkdv_kernel": 2 * f_fwd,
+                        "bwd_dq_kernel": 1.5 * f_fwd}
+    dom = max(per_kernel_flops, key=lambda kname: ms[kname])
+    achieved = per_kernel_flops[dom] / (ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(dom, WORKLOAD),
+                "avg_launch_ms": round(ms[dom], 4)}
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": B, "Hq": Hq, "Hkv": Hkv, "N": Nq, "d": d,
+                   "causal": causal, "step": "fwd + recompute bwd"},
+        "pct_bf16_peak": round(value / PEAK_BF16_TFLOPS * 100, 2),
+        "roofline": roofline,
+        "phases_ms": {kname: round(t, 4) for kname, t in ms.items()},
+        "phase_tflops": {"fwd": round(f_fwd / ms["fwd_bf16_kernel"] / 1e9, 1),
+                         "bwd": round(2.5 * f_fwd / (ms["bwd_pre_kernel"] + ms["bwd_dkdv_kernel"]
+                                                     + ms["bwd_dq_kernel"]) / 1e9, 1)},
+    }
+    if not args.profile and not args.no_extra:
+        log("extra workloads")
+        rec["extra"] = extras(torch, fa)
+    if not args.profile and not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        rec["cpu_baseline"] = cpu_baseline(inp)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -81,8 +81,7 @@ __device__ __forceinline__ float lse2_of(const BwdParams& p, size_t idx, bool va
 // ---------------------------------------------------------------------------------
 template <int D, int BMQ>
 struct DkdvTile {
-  static constexpr int STR = D + 8;
-  static constexpr int TILE = BMQ * STR;
+  static constexpr int TILE = TileLayout<D>::elems(BMQ);
   static constexpr int LPT = BMQ * D / 8 / 256;
   static_assert(LPT * 256 * 8 == BMQ * D, "tile must split evenly");
 };
@@ -90,7 +89,8 @@ struct DkdvTile {
 template <int D, int BMQ, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) {
   using T = DkdvTile<D, BMQ>;
-  constexpr int STR = T::STR, LPT = T::LPT, CPR = D / 8;
+  using TL = TileLayout<D>;
+  constexpr int LPT = T::LPT, CPR = D / 8;
   constexpr int NDC = D / 16, NCB = D / 32, NQS = BMQ / 32;
   constexpr int BNK = 128;
 
@@ -142,17 +142,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     const int h = kvh * p.g + s / per_head;
     const int i0 = (qb0 + s % per_head) * BMQ;
     const size_t hbase = (size_t)(b * p.Hq + h) * p.Nq;
+    // rows past Nq re-read the last row; their LSE is +inf, so P = dS = 0 for them
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      const int qi = i0 + row;
-      if (qi < p.Nq) {
-        qpre[i] = ((const u32x4_t*)(p.q + (hbase + qi) * D))[col];
-        dopre[i] = ((const u32x4_t*)(p.dO + (hbase + qi) * D))[col];
-      } else {
-        qpre[i] = u32x4_t{0, 0, 0, 0};
-        dopre[i] = u32x4_t{0, 0, 0, 0};
-      }
+      const int qi = min(i0 + row, p.Nq - 1);
+      qpre[i] = ((const u32x4_t*)(p.q + (hbase + qi) * D))[col];
+      dopre[i] = ((const u32x4_t*)(p.dO + (hbase + qi) * D))[col];
     }
     if (tid < BMQ) {
       const int qi = i0 + tid;
@@ -166,8 +162,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      *(FA_LDS u32x4_t*)(Qs + row * STR + col * 8) = qpre[i];
-      *(FA_LDS u32x4_t*)(Os + row * STR + col * 8) = dopre[i];
+      *(FA_LDS u32x4_t*)(Qs + TL::off(row, col * 8)) = qpre[i];
+      *(FA_LDS u32x4_t*)(Os + TL::off(row, col * 8)) = dopre[i];
     }
     if (tid < BMQ) {
       svec[buf * 2 * BMQ + tid] = lpre;
@@ -200,12 +196,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       // every (query, key) pair of this wave's 32x32 block is above the diagonal
       if (CAUSAL && ib + 31 + p.causal_off < wkey0) continue;
       f32x16_t S = zero16(), dP = zero16();
-      const uint16_t* qp = Qs + (32 * qs + l32) * STR + 8 * hi;
-      const uint16_t* op = Os + (32 * qs + l32) * STR + 8 * hi;
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
-        S = mfma32x32x16(lds_read8(qp + 16 * dc), kreg[dc], S);
-        dP = mfma32x32x16(lds_read8(op + 16 * dc), vreg[dc], dP);
+        const int off = TL::off(32 * qs + l32, 16 * dc + 8 * hi);
+        S = mfma32x32x16(lds_read8(Qs + off), kreg[dc], S);
+        dP = mfma32x32x16(lds_read8(Os + off), vreg[dc], dP);
       }
       const bool need_mask = CAUSAL && (ib + p.causal_off < wkey0 + 31);
       uint32_t ppk[8], dspk[8];
@@ -234,13 +229,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pu);
         const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
         const int rowb = 32 * qs + 16 * kk + tr_row;
-        const uint16_t* otr = Os + rowb * STR + tr_col;
-        const uint16_t* qtr = Qs + rowb * STR + tr_col;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const bf16x8_t ao = join8(lds_read_tr4(otr + 32 * cb), lds_read_tr4(otr + 8 * STR + 32 * cb));
+          const int o0 = TL::off(rowb, tr_col + 32 * cb), o1 = TL::off(rowb + 8, tr_col + 32 * cb);
+          const bf16x8_t ao = join8(lds_read_tr4(Os + o0), lds_read_tr4(Os + o1));
           dvacc[cb] = mfma32x32x16(ao, pb, dvacc[cb]);
-          const bf16x8_t aq = join8(lds_read_tr4(qtr + 32 * cb), lds_read_tr4(qtr + 8 * STR + 32 * cb));
+          const bf16x8_t aq = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o1));
           dkacc[cb] = mfma32x32x16(aq, db, dkacc[cb]);
         }
       }
@@ -271,8 +265,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
 // ---------------------------------------------------------------------------------
 template <int D, int BN>
 struct DqTile {
-  static constexpr int STR = D + 8;
-  static constexpr int TILE = BN * STR;
+  static constexpr int TILE = TileLayout<D>::elems(BN);
   static constexpr int LPT = BN * D / 8 / 256;
   static_assert(LPT * 256 * 8 == BN * D, "tile must split evenly");
 };
@@ -280,7 +273,8 @@ struct DqTile {
 template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   using T = DqTile<D, BN>;
-  constexpr int STR = T::STR, LPT = T::LPT, CPR = D / 8;
+  using TL = TileLayout<D>;
+  constexpr int LPT = T::LPT, CPR = D / 8;
   constexpr int NDC = D / 16, NCB = D / 32, NKB = BN / 32;
   constexpr int BM = 128;
 
@@ -328,17 +322,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   u32x4_t kpre[LPT], vpre[LPT];
   auto gload = [&](int t) {
     const int j0 = t * BN;
+    // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      const int j = j0 + row;
-      if (j < p.Nk) {
-        kpre[i] = ((const u32x4_t*)(Kg + (size_t)j * D))[col];
-        vpre[i] = ((const u32x4_t*)(Vg + (size_t)j * D))[col];
-      } else {
-        kpre[i] = u32x4_t{0, 0, 0, 0};
-        vpre[i] = u32x4_t{0, 0, 0, 0};
-      }
+      const int j = min(j0 + row, p.Nk - 1);
+      kpre[i] = ((const u32x4_t*)(Kg + (size_t)j * D))[col];
+      vpre[i] = ((const u32x4_t*)(Vg + (size_t)j * D))[col];
     }
   };
   auto lstore = [&](int buf) {
@@ -347,8 +337,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      *(FA_LDS u32x4_t*)(Ks + row * STR + col * 8) = kpre[i];
-      *(FA_LDS u32x4_t*)(Vs + row * STR + col * 8) = vpre[i];
+      *(FA_LDS u32x4_t*)(Ks + TL::off(row, col * 8)) = kpre[i];
+      *(FA_LDS u32x4_t*)(Vs + TL::off(row, col * 8)) = vpre[i];
     }
   };
 
@@ -375,12 +365,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
       for (int kb = 0; kb < NKB; ++kb) {
         S[kb] = zero16();
         dP[kb] = zero16();
-        const uint16_t* kp = Ks + (32 * kb + l32) * STR + 8 * hi;
-        const uint16_t* vp = Vs + (32 * kb + l32) * STR + 8 * hi;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
-          S[kb] = mfma32x32x16(lds_read8(kp + 16 * dc), qreg[dc], S[kb]);
-          dP[kb] = mfma32x32x16(lds_read8(vp + 16 * dc), doreg[dc], dP[kb]);
+          const int off = TL::off(32 * kb + l32, 16 * dc + 8 * hi);
+          S[kb] = mfma32x32x16(lds_read8(Ks + off), qreg[dc], S[kb]);
+          dP[kb] = mfma32x32x16(lds_read8(Vs + off), doreg[dc], dP[kb]);
         }
       }
       const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && (j0 + BN - 1 > q0 + 32 * w + p.causal_off));
@@ -408,10 +397,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
         for (int kk = 0; kk < 2; ++kk) {
           const u32x4_t du = {dspk[kb][4 * kk], dspk[kb][4 * kk + 1], dspk[kb][4 * kk + 2], dspk[kb][4 * kk + 3]};
           const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
-          const uint16_t* ktr = Ks + (32 * kb + 16 * kk + tr_row) * STR + tr_col;
+          const int kr = 32 * kb + 16 * kk + tr_row;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            const bf16x8_t a = join8(lds_read_tr4(ktr + 32 * cb), lds_read_tr4(ktr + 8 * STR + 32 * cb));
+            const bf16x8_t a = join8(lds_read_tr4(Ks + TL::off(kr, tr_col + 32 * cb)),
+                                     lds_read_tr4(Ks + TL::off(kr + 8, tr_col + 32 * cb)));
             dqacc[cb] = mfma32x32x16(a, db, dqacc[cb]);
           }
         }
@@ -434,10 +424,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   }
 }
 
+// stage 0: D = rowsum(dO * O); stage 1: dK, dV; stage 2: dQ; stage -1: all three.
 template <int D, int BMQ, int BN, bool CAUSAL>
-hipError_t run(const BwdParams& p, int B, hipStream_t st) {
-  const int rows = B * p.Hq * p.Nq;
-  {
+hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
+  if (stage == -1 || stage == 0) {
+    const int rows = B * p.Hq * p.Nq;
     constexpr int RPB = 256 / (D / 8);
     int nb = (rows + RPB - 1) / RPB;
     if (nb > 65536) nb = 65536;
@@ -445,7 +436,7 @@ hipError_t run(const BwdParams& p, int B, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (stage == -1 || stage == 1) {
     const int nkb = (p.Nk + 127) / 128;
     const long long n = (long long)nkb * p.Hkv * B;
     if (n > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -453,13 +444,15 @@ hipError_t run(const BwdParams& p, int B, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (stage == -1 || stage == 2) {
     const int nqb = (p.Nq + 127) / 128;
     const long long n = (long long)nqb * p.Hq * B;
     if (n > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nqb);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -467,7 +460,7 @@ hipError_t run(const BwdParams& p, int B, hipStream_t st) {
 hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse,
                       uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec,
-                      const AttnShape& s, hipStream_t st) {
+                      const AttnShape& s, int stage, hipStream_t st) {
   BwdParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dvec = dvec;
@@ -477,9 +470,9 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
   switch (s.d) {
-    case 64: return c ? run<64, 64, 64, true>(p, s.B, st) : run<64, 64, 64, false>(p, s.B, st);
-    case 128: return c ? run<128, 64, 64, true>(p, s.B, st) : run<128, 64, 64, false>(p, s.B, st);
-    case 256: return c ? run<256, 32, 32, true>(p, s.B, st) : run<256, 32, 32, false>(p, s.B, st);
+    case 64: return c ? run<64, 64, 64, true>(p, s.B, stage, st) : run<64, 64, 64, false>(p, s.B, stage, st);
+    case 128: return c ? run<128, 64, 64, true>(p, s.B, stage, st) : run<128, 64, 64, false>(p, s.B, stage, st);
+    case 256: return c ? run<256, 32, 32, true>(p, s.B, stage, st) : run<256, 32, 32, false>(p, s.B, stage, st);
     default: return hipErrorInvalidValue;
   }
 }

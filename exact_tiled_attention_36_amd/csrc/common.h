@@ -82,6 +82,33 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS layout of a [rows][D] bf16 tile. Two access patterns hit every tile: 16-byte
+// row reads (lanes 0..31 read 32 different rows at one column chunk, MFMA A operand)
+// and transposed reads (each 16-lane group reads 4 consecutive rows x 32 bytes,
+// ds_read_b64_tr_b16). With a plain power-of-two row stride both serialize on the
+// same banks. The default layout pads every row by 32 bytes and shifts rows 4..7
+// of every 8 by another 16 bytes, so that 8 consecutive rows start on 8 different
+// 16-byte bank slots (row reads) and 4 consecutive rows x 32 bytes cover 8 distinct
+// slots (transposed reads); all offsets stay "per-lane base + constant". The
+// alternative (FA_LDS_XOR) keeps rows unpadded and XORs the 16-byte chunk index with
+// S[r % 4] ^ (r / 4 % 4), S = {0, 6, 10, 12}, conflict-free for 32- and 64-bank LDS
+// models at the price of address arithmetic per read.
+#ifndef FA_LDS_XOR
+#define FA_LDS_XOR 0
+#endif
+template <int D>
+struct TileLayout {
+  static constexpr int elems(int rows) { return rows * (D + 16) + 8; }
+  __device__ __forceinline__ static int off(int r, int e) {
+#if FA_LDS_XOR
+    const int f = ((0xCA60 >> ((r & 3) << 2)) & 15) ^ ((r >> 2) & 3);
+    return r * D + ((((e >> 3) ^ f) & (D / 8 - 1)) << 3) + (e & 7);
+#else
+    return r * (D + 16) + (((r >> 2) & 1) << 3) + e;
+#endif
+  }
+};
+
 // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2). Map the
 // hardware id to a logical id so that consecutive logical ids run on one XCD.
 __device__ __forceinline__ int xcd_remap(int hw, int n) {

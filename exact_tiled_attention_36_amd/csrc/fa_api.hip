@@ -66,6 +66,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: problem exceeds the library's index range";
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_STAGE: return "FA_ERR_STAGE: backward stage must be 0, 1 or 2";
     default: return "unknown fa status code";
   }
 }
@@ -144,10 +145,11 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   return align256((size_t)B * Hq * Nq * sizeof(float));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-           const float* lse, void* dq, void* dk, void* dv, void* workspace,
-           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-           int causal, void* stream) {
+static int bwd_common(const void* q, const void* k, const void* v, const void* o,
+                      const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, float scale, int causal, int stage,
+                      void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
   if (st != FA_OK) return st;
@@ -161,7 +163,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return launch_status(fa::launch_bwd(
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
       (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, (float*)workspace,
-      shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), (hipStream_t)stream));
+      shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), stage, (hipStream_t)stream));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, void* stream) {
+  return bwd_common(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                    Nq, Nk, d, scale, causal, -1, stream);
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d, float scale, int causal, void* stream) {
+  if (stage < 0 || stage > 2) return FA_ERR_STAGE;
+  return bwd_common(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                    Nq, Nk, d, scale, causal, stage, stream);
 }
 
 }  // extern "C"

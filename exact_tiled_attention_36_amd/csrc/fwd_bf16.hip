@@ -32,6 +32,10 @@
 namespace fa {
 namespace {
 
+// Headroom (in log2 units) the running max may lag behind the true row max before
+// the accumulators are rescaled: weights stay below 2^8, far inside fp32/bf16 range.
+constexpr float kRescaleSlack = 8.f;
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -45,8 +49,7 @@ struct FwdParams {
 template <int D, int BN>
 struct FwdTile {
   static constexpr int BM = 128;
-  static constexpr int STR = D + 8;                 // LDS row stride (elements)
-  static constexpr int TILE = BN * STR;             // elements per K or V tile
+  static constexpr int TILE = TileLayout<D>::elems(BN);  // elements per K or V tile
   static constexpr int LPT = BN * D / 8 / 256;      // 16-byte chunks per thread per tensor
   static constexpr int LDS_BYTES = 2 * 2 * TILE * 2;
   static_assert(LPT * 256 * 8 == BN * D, "tile must split evenly over 256 threads");
@@ -55,7 +58,8 @@ struct FwdTile {
 template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D, BN>;
-  constexpr int BM = T::BM, STR = T::STR, LPT = T::LPT;
+  using TL = TileLayout<D>;
+  constexpr int BM = T::BM, LPT = T::LPT;
   constexpr int NKB = BN / 32;   // 32-key sub-blocks per tile
   constexpr int NDC = D / 16;    // 16-wide chunks of d (reduction of S)
   constexpr int NCB = D / 32;    // 32-wide column blocks of O
@@ -101,19 +105,16 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
   const float c2 = p.scale_log2;
 
   u32x4_t kreg[LPT], vreg[LPT];
+  // Rows past the last key re-read the last key row: always finite, and masked to
+  // zero weight before they can contribute, so no branch is needed here.
   auto gload = [&](int t) {
     const int j0 = t * BN;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      const int j = j0 + row;
-      if (j < p.Nk) {
-        kreg[i] = ((const u32x4_t*)(Kg + (size_t)j * D))[col];
-        vreg[i] = ((const u32x4_t*)(Vg + (size_t)j * D))[col];
-      } else {
-        kreg[i] = u32x4_t{0, 0, 0, 0};
-        vreg[i] = u32x4_t{0, 0, 0, 0};
-      }
+      const int j = min(j0 + row, p.Nk - 1);
+      kreg[i] = ((const u32x4_t*)(Kg + (size_t)j * D))[col];
+      vreg[i] = ((const u32x4_t*)(Vg + (size_t)j * D))[col];
     }
   };
   auto lstore = [&](int buf) {
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      *(FA_LDS u32x4_t*)(Ks + row * STR + col * 8) = kreg[i];
-      *(FA_LDS u32x4_t*)(Vs + row * STR + col * 8) = vreg[i];
+      *(FA_LDS u32x4_t*)(Ks + TL::off(row, col * 8)) = kreg[i];
+      *(FA_LDS u32x4_t*)(Vs + TL::off(row, col * 8)) = vreg[i];
     }
   };
 
@@ -148,12 +149,12 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
     // S^T = K Q^T for this wave's 32 queries and the tile's BN keys.
     f32x16_t s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = zero16();
-      const uint16_t* kp = Ks + (32 * kb + l32) * STR + 8 * hi;
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) s[kb] = mfma32x32x16(lds_read8(kp + 16 * dc), qreg[dc], s[kb]);
-    }
+    for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = mfma32x32x16(lds_read8(Ks + TL::off(32 * kb + l32, 16 * dc + 8 * hi)), qreg[dc], s[kb]);
 
     const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && (j0 + BN - 1 > q0 + p.causal_off));
     if (need_mask) {
@@ -172,11 +173,22 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m, mx * c2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
+    mx = xhalf_max(mx) * c2;
+    // Lazy rescale: the exponent base m only moves when some row of the wave sees a
+    // score more than kRescaleSlack (log2 units) above it. Otherwise the stale base is
+    // kept and weights up to 2^kRescaleSlack are accumulated; the final O / l and
+    // lse = m + log l use the same base, so the result is unchanged.
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
+      lsum *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      m = m_new;
+    }
+    const float m_use = (m == -INFINITY) ? 0.f : m;
 
     float rs = 0.f;
     uint32_t pk[NKB][8];
@@ -189,11 +201,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
         rs += p0 + p1;
         pk[kb][r >> 1] = pack_bf16x2(p0, p1);
       }
-    lsum = fmaf(lsum, alpha, rs);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+    lsum += rs;
 
     // O^T += V^T P^T, one 16-key chunk at a time.
 #pragma unroll
@@ -202,10 +210,11 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
       for (int kk = 0; kk < 2; ++kk) {
         const u32x4_t bu = {pk[kb][4 * kk], pk[kb][4 * kk + 1], pk[kb][4 * kk + 2], pk[kb][4 * kk + 3]};
         const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bu);
-        const uint16_t* vp = Vs + (32 * kb + 16 * kk + tr_row) * STR + tr_col;
+        const int vr = 32 * kb + 16 * kk + tr_row;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const bf16x8_t a = join8(lds_read_tr4(vp + 32 * cb), lds_read_tr4(vp + 8 * STR + 32 * cb));
+          const bf16x8_t a = join8(lds_read_tr4(Vs + TL::off(vr, tr_col + 32 * cb)),
+                                   lds_read_tr4(Vs + TL::off(vr + 8, tr_col + 32 * cb)));
           oacc[cb] = mfma32x32x16(a, bop, oacc[cb]);
         }
       }

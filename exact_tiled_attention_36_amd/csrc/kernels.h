@@ -27,9 +27,10 @@ hipError_t launch_fwd_splitkv(const uint16_t* q, const uint16_t* k, const uint16
                               int splits, const AttnShape& s, hipStream_t st);
 
 // Backward. `dvec` [B,Hq,Nq] fp32 scratch for D_i = rowsum(dO * O).
+// stage: -1 all, 0 D preprocess, 1 dK/dV, 2 dQ.
 hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse,
                       uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec,
-                      const AttnShape& s, hipStream_t st);
+                      const AttnShape& s, int stage, hipStream_t st);
 
 }  // namespace fa

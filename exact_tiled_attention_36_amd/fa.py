@@ -34,6 +34,8 @@ _SIGNATURES = {
                        + [_c_float, _c_int, _c_int, _vp, _c_size, _vp]),
     "fa_bwd_workspace_bytes": (_c_size, [_c_int] * 6),
     "fa_bwd": (_c_int, [_vp] * 10 + [_c_size] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "fa_bwd_stage": (_c_int, [_c_int] + [_vp] * 10 + [_c_size] + [_c_int] * 6
+                     + [_c_float, _c_int, _vp]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -46,13 +48,16 @@ class FAError(RuntimeError):
 
 
 def load(path: Optional[str] = None, require_torch: bool = True):
-    """Load libfa.so once and attach the C signatures. Raises if it is not built."""
+    """Load libfa.so once and attach the C signatures. Raises if it is not built.
+
+    The library next to this file is used unless ``path`` or the environment variable
+    FA_LIBRARY names another build of the same sources."""
     global _lib
     if _lib is not None and path is None:
         return _lib
     if require_torch:
         import torch  # noqa: F401  (loads the HIP runtime the library must share)
-    p = path or LIB_PATH
+    p = path or os.environ.get("FA_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is not built; run __graft_entry__.build() or "
                            "python -m exact_tiled_attention_36_amd.build")
@@ -156,8 +161,11 @@ def bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d) -> int:
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
-        dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV (bf16) by recomputation from the forward's O and LSE."""
+        dq=None, dk=None, dv=None, workspace=None, stage: int = -1):
+    """dQ, dK, dV (bf16) by recomputation from the forward's O and LSE.
+
+    ``stage`` -1 runs the whole backward (fa_bwd); 0, 1, 2 run one kernel stage
+    (fa_bwd_stage: D preprocess, dK/dV, dQ) with the same buffers."""
     import torch
     lib = load()
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
@@ -173,9 +181,12 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     nbytes = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                    workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, Nq, Nk, d, sc,
-                    int(bool(causal)), _stream(q.device))
-    _check("fa_bwd", st)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, Nq, Nk, d, sc,
+            int(bool(causal)), _stream(q.device))
+    if stage == -1:
+        _check("fa_bwd", lib.fa_bwd(*args))
+    else:
+        _check("fa_bwd_stage", lib.fa_bwd_stage(int(stage), *args))
     return dq, dk, dv

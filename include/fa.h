@@ -58,7 +58,8 @@ enum {
   FA_ERR_LAUNCH = -7,     /* the HIP runtime rejected a kernel launch            */
   FA_ERR_TOO_LARGE = -8,  /* an index would overflow 32/64-bit addressing limits */
   FA_ERR_SPLITS = -9,     /* num_splits out of range                             */
-  FA_ERR_SCALE = -10      /* scale is not a finite number > 0                    */
+  FA_ERR_SCALE = -10,     /* scale is not a finite number > 0                    */
+  FA_ERR_STAGE = -11      /* fa_bwd_stage: stage not in {0, 1, 2}                */
 };
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -121,6 +122,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
            float scale, int causal, void* stream);
+
+/*
+ * One stage of fa_bwd, same arguments plus `stage`, for callers that schedule or
+ * time the three kernels separately. fa_bwd == stage 0, then 1, then 2 on one stream.
+ *   stage 0: D_i = sum_c dO_ic o_ic into the workspace (must run first);
+ *   stage 1: dk and dv (reads D);
+ *   stage 2: dq (reads D).
+ * Stages 1 and 2 are independent of each other. Returns FA_ERR_STAGE for other values.
+ */
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d, float scale, int causal, void* stream);
 
 #ifdef __cplusplus
 }
