@@ -82,32 +82,73 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS layout of a [rows][D] bf16 tile. Two access patterns hit every tile: 16-byte
-// row reads (lanes 0..31 read 32 different rows at one column chunk, MFMA A operand)
-// and transposed reads (each 16-lane group reads 4 consecutive rows x 32 bytes,
-// ds_read_b64_tr_b16). With a plain power-of-two row stride both serialize on the
-// same banks. The default layout pads every row by 32 bytes and shifts rows 4..7
-// of every 8 by another 16 bytes, so that 8 consecutive rows start on 8 different
-// 16-byte bank slots (row reads) and 4 consecutive rows x 32 bytes cover 8 distinct
-// slots (transposed reads); all offsets stay "per-lane base + constant". The
-// alternative (FA_LDS_XOR) keeps rows unpadded and XORs the 16-byte chunk index with
-// S[r % 4] ^ (r / 4 % 4), S = {0, 6, 10, 12}, conflict-free for 32- and 64-bank LDS
-// models at the price of address arithmetic per read.
-#ifndef FA_LDS_XOR
-#define FA_LDS_XOR 0
-#endif
+// LDS layout of a [rows][D] bf16 tile (rows a multiple of 16). Every tile is read
+// two ways: 16-byte row reads (lanes 0..31 read 32 different rows at one column
+// chunk: MFMA A operands) and transposed reads (each 16-lane group reads 4
+// consecutive rows x 32 bytes: ds_read_b64_tr_b16). Measured bank-conflict counts on
+// gfx950 follow a model of 64 four-byte banks serving 16 lanes of a 16-byte read or
+// 32 lanes of an 8-byte read per cycle. In units of 16-byte slots (16 per bank
+// cycle), row r is started at slot 4*(r%4) + (r/4)%4 (mod 16): 16 consecutive rows
+// then start on 16 different slots (row reads), and 4 consecutive rows x 64 bytes
+// cover 16 different slots (transposed reads of two 16-lane groups). Rows stay
+// contiguous (for d=64, row pairs), so whole 256-byte pieces can be filled by one
+// direct global->LDS load, and every offset is "per-lane row base + constant".
+// Padding: 1 KiB per 16 rows (d >= 128) or 512 bytes per 16 rows (d = 64).
 template <int D>
 struct TileLayout {
-  static constexpr int elems(int rows) { return rows * (D + 16) + 8; }
-  __device__ __forceinline__ static int off(int r, int e) {
-#if FA_LDS_XOR
-    const int f = ((0xCA60 >> ((r & 3) << 2)) & 15) ^ ((r >> 2) & 3);
-    return r * D + ((((e >> 3) ^ f) & (D / 8 - 1)) << 3) + (e & 7);
-#else
-    return r * (D + 16) + (((r >> 2) & 1) << 3) + e;
-#endif
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
+  static constexpr int elems(int rows) {
+    return D == 64 ? (rows / 16) * 1280 : (rows / 16) * (16 * D + 512);
   }
+  // element offset of row r
+  __device__ __forceinline__ static int row(int r) {
+    if constexpr (D == 64) {
+      const int m = r >> 1;  // row pair, stored contiguously
+      const int a = 4 * (m & 1) + 9 * ((m >> 1) & 3) + 32 * (m >> 3);
+      return m * 128 + 8 * a + 64 * (r & 1);
+    } else {
+      const int sl = 4 * (r & 3) + 17 * ((r >> 2) & 3) + 64 * (r >> 4);
+      return r * D + 8 * sl;
+    }
+  }
+  __device__ __forceinline__ static int off(int r, int e) { return row(r) + e; }
 };
+
+// Asynchronous copy of a [ROWS][D] bf16 tile (global rows j0.. of G, clamped to
+// nrows-1) into an LDS tile, by direct global->LDS loads of 4 bytes per lane: each
+// wave instruction fills one contiguous 256-byte piece (128 elements). The NW waves of
+// the workgroup share the pieces; `wu` is the wave index made wave-uniform
+// (readfirstlane), so piece and row arithmetic stays scalar and the only per-lane
+// term is the lane's byte offset. Completion is tracked by vmcnt: wait_vmem() and a
+// barrier must follow before any wave reads the tile.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_load_async(const uint16_t* G, int j0, int nrows,
+                                                uint16_t* lds, int wu, int lane) {
+  constexpr int NSEG = ROWS * D / 128;
+  static_assert(NSEG % NW == 0, "pieces must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < NSEG / NW; ++i) {
+    const int k = wu + NW * i;  // piece index (uniform)
+    const uint16_t* src;
+    uint16_t* dst;
+    if constexpr (D == 64) {
+      // piece k = rows 2k and 2k+1, contiguous in global memory and in LDS
+      const int r = 2 * k + (lane >> 5);
+      src = G + (size_t)min(j0 + r, nrows - 1) * D + 2 * (lane & 31);
+      dst = lds + TileLayout<D>::row(2 * k);
+    } else {
+      constexpr int PPR = D / 128;  // pieces per row
+      const int r = k / PPR, c0 = (k % PPR) * 128;
+      src = G + (size_t)min(j0 + r, nrows - 1) * D + c0 + 2 * lane;
+      dst = lds + TileLayout<D>::row(r) + c0;
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (FA_LDS void*)dst, 4, 0, 0);
+  }
+}
+
+// Wait until this wave's vector memory operations (including direct LDS loads) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2). Map the
 // hardware id to a logical id so that consecutive logical ids run on one XCD.
