@@ -40,7 +40,8 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dvec;
+  float* dvec;   // D_i, [B, Hq, Nq]
+  float* lse2v;  // lse_i * log2(e), +inf for rows that saw no key, [B, Hq, Nq]
   int Hq, Hkv, Nq, Nk, g, causal_off;
   float scale, scale_log2;
 };
@@ -64,7 +65,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int rows) {
     }
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-    if (sub == 0) p.dvec[row] = acc;
+    if (sub == 0) {
+      p.dvec[row] = acc;
+      const float l = p.lse[row];
+      p.lse2v[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
   }
 }
 
@@ -74,6 +79,16 @@ __device__ __forceinline__ float lse2_of(const BwdParams& p, size_t idx, bool va
   if (!valid) return INFINITY;
   const float l = p.lse[idx];
   return l == -INFINITY ? INFINITY : l * kLog2e;
+}
+
+// Asynchronous copy of n consecutive floats (n <= 64; indices clamped to last) into LDS
+// by one wave: one direct global->LDS load of 4 bytes per lane. The LDS destination
+// must have room for 64 floats.
+__device__ __forceinline__ void vec_load_async(const float* G, int i0, int last, float* lds,
+                                               int lane) {
+  const float* src = G + min(i0 + lane, last);
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (FA_LDS void*)lds, 4, 0, 0);
 }
 
 // ---------------------------------------------------------------------------------
@@ -263,24 +278,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
 // ---------------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------------
-template <int D, int BN>
-struct DqTile {
-  static constexpr int TILE = TileLayout<D>::elems(BN);
-  static constexpr int LPT = BN * D / 8 / 256;
-  static_assert(LPT * 256 * 8 == BN * D, "tile must split evenly");
-};
-
-template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
-  using T = DqTile<D, BN>;
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   using TL = TileLayout<D>;
-  constexpr int LPT = T::LPT, CPR = D / 8;
+  constexpr int TILE = TL::elems(BN);
   constexpr int NDC = D / 16, NCB = D / 32, NKB = BN / 32;
-  constexpr int BM = 128;
+  constexpr int BM = 32 * NW;    // query rows per workgroup (one 32-row block per wave)
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * T::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int qb = L % nqb;
@@ -288,7 +296,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   if (CAUSAL) qb = nqb - 1 - qb;
   const int h = bh % p.Hq, b = bh / p.Hq, kvh = h / p.g;
   const int q0 = qb * BM;
-  const int qrow = q0 + 32 * w + l32;
+  const int w0 = q0 + 32 * wu;
+  const int qrow = w0 + l32;
   const bool qvalid = qrow < p.Nq;
   const size_t rowidx = (size_t)(b * p.Hq + h) * p.Nq + (qvalid ? qrow : p.Nq - 1);
 
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
       doreg[dc] = __builtin_bit_cast(bf16x8_t, os[2 * dc]);
     }
   }
-  const float lse2 = lse2_of(p, rowidx, qvalid);
+  const float lse2 = qvalid ? p.lse2v[rowidx] : INFINITY;
   const float Dv = qvalid ? p.dvec[rowidx] : 0.f;
 
   const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
@@ -319,60 +328,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   for (int cb = 0; cb < NCB; ++cb) dqacc[cb] = zero16();
   const float c2 = p.scale_log2;
 
-  u32x4_t kpre[LPT], vpre[LPT];
-  auto gload = [&](int t) {
-    const int j0 = t * BN;
-    // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      const int j = min(j0 + row, p.Nk - 1);
-      kpre[i] = ((const u32x4_t*)(Kg + (size_t)j * D))[col];
-      vpre[i] = ((const u32x4_t*)(Vg + (size_t)j * D))[col];
-    }
+  auto Kb = [&](int i) { return smem + (i & 1) * TILE; };
+  auto Vb = [&](int i) { return smem + (2 + (i & 1)) * TILE; };
+  // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
+  auto load = [&](const uint16_t* G, int t, uint16_t* dst) {
+    tile_load_async<D, BN, NW>(G, t * BN, p.Nk, dst, wu, lane);
   };
-  auto lstore = [&](int buf) {
-    uint16_t* Ks = smem + buf * 2 * T::TILE;
-    uint16_t* Vs = Ks + T::TILE;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      *(FA_LDS u32x4_t*)(Ks + TL::off(row, col * 8)) = kpre[i];
-      *(FA_LDS u32x4_t*)(Vs + TL::off(row, col * 8)) = vpre[i];
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
 
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int wq_last = q0 + 32 * w + 31;  // last query of this wave
+  const int wlim = w0 + 31 + p.causal_off;  // last key any row of this wave sees
 
+  if (ntiles > 0) {
+    load(Kg, 0, Kb(0));
+    load(Vg, 0, Vb(0));
+    wait_vmem();
+    __syncthreads();
+  }
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    const uint16_t* Ks = smem + buf * 2 * T::TILE;
-    const uint16_t* Vs = Ks + T::TILE;
+    if (t + 1 < ntiles) {
+      load(Kg, t + 1, Kb(t + 1));
+      load(Vg, t + 1, Vb(t + 1));
+    }
+    const uint16_t* Ks = Kb(t);
+    const uint16_t* Vs = Vb(t);
     const int j0 = t * BN;
     // skip tiles that lie wholly above this wave's part of the diagonal
-    if (!CAUSAL || j0 <= wq_last + p.causal_off) {
+    if (!CAUSAL || j0 <= wlim) {
       f32x16_t S[NKB], dP[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         S[kb] = zero16();
         dP[kb] = zero16();
+      }
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
+      for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
           const int off = TL::off(32 * kb + l32, 16 * dc + 8 * hi);
           S[kb] = mfma32x32x16(lds_read8(Ks + off), qreg[dc], S[kb]);
           dP[kb] = mfma32x32x16(lds_read8(Vs + off), doreg[dc], dP[kb]);
         }
-      }
-      const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && (j0 + BN - 1 > q0 + 32 * w + p.causal_off));
+      const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && (j0 + BN - 1 > w0 + p.causal_off));
       const int lim = CAUSAL ? qrow + p.causal_off : 0x7fffffff;
       uint32_t dspk[NKB][8];
 #pragma unroll
@@ -406,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
           }
         }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -425,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
 }
 
 // stage 0: D = rowsum(dO * O); stage 1: dK, dV; stage 2: dQ; stage -1: all three.
-template <int D, int BMQ, int BN, bool CAUSAL>
+template <int D, int BMQ, int BN, int NWQ, bool CAUSAL>
 hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
   if (stage == -1 || stage == 0) {
     const int rows = B * p.Hq * p.Nq;
@@ -445,10 +442,10 @@ hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (stage == -1 || stage == 2) {
-    const int nqb = (p.Nq + 127) / 128;
+    const int nqb = (p.Nq + 32 * NWQ - 1) / (32 * NWQ);
     const long long n = (long long)nqb * p.Hq * B;
     if (n > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nqb);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, NWQ, CAUSAL>), dim3((int)n), dim3(64 * NWQ), 0, st, p, nqb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -462,6 +459,7 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec,
                       const AttnShape& s, int stage, hipStream_t st) {
   BwdParams p;
+  p.lse2v = dvec + (size_t)s.B * s.Hq * s.Nq;
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dvec = dvec;
   p.Hq = s.Hq; p.Hkv = s.Hkv; p.Nq = s.Nq; p.Nk = s.Nk; p.g = s.Hq / s.Hkv;
@@ -470,9 +468,9 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
   switch (s.d) {
-    case 64: return c ? run<64, 64, 64, true>(p, s.B, stage, st) : run<64, 64, 64, false>(p, s.B, stage, st);
-    case 128: return c ? run<128, 64, 64, true>(p, s.B, stage, st) : run<128, 64, 64, false>(p, s.B, stage, st);
-    case 256: return c ? run<256, 32, 32, true>(p, s.B, stage, st) : run<256, 32, 32, false>(p, s.B, stage, st);
+    case 64: return c ? run<64, 64, 64, 8, true>(p, s.B, stage, st) : run<64, 64, 64, 8, false>(p, s.B, stage, st);
+    case 128: return c ? run<128, 64, 64, 8, true>(p, s.B, stage, st) : run<128, 64, 64, 8, false>(p, s.B, stage, st);
+    case 256: return c ? run<256, 32, 32, 4, true>(p, s.B, stage, st) : run<256, 32, 32, 4, false>(p, s.B, stage, st);
     default: return hipErrorInvalidValue;
   }
 }

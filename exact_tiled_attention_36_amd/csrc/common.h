@@ -117,7 +117,7 @@ struct TileLayout {
 // Asynchronous copy of a [ROWS][D] bf16 tile (global rows j0.. of G, clamped to
 // nrows-1) into an LDS tile, by direct global->LDS loads of 4 bytes per lane: each
 // wave instruction fills one contiguous 256-byte piece (128 elements). The NW waves of
-// the workgroup share the pieces; `wu` is the wave index made wave-uniform
+// the workgroup take every NW-th piece; `wu` is the wave index made wave-uniform
 // (readfirstlane), so piece and row arithmetic stays scalar and the only per-lane
 // term is the lane's byte offset. Completion is tracked by vmcnt: wait_vmem() and a
 // barrier must follow before any wave reads the tile.

@@ -142,7 +142,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
-  return align256((size_t)B * Hq * Nq * sizeof(float));
+  return align256(2 * (size_t)B * Hq * Nq * sizeof(float));
 }
 
 static int bwd_common(const void* q, const void* k, const void* v, const void* o,

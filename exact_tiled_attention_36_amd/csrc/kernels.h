@@ -26,7 +26,8 @@ hipError_t launch_fwd_splitkv(const uint16_t* q, const uint16_t* k, const uint16
                               uint16_t* o, float* lse, float* part_o, float* part_lse,
                               int splits, const AttnShape& s, hipStream_t st);
 
-// Backward. `dvec` [B,Hq,Nq] fp32 scratch for D_i = rowsum(dO * O).
+// Backward. `dvec` is fp32 scratch of 2 * B*Hq*Nq floats: D_i = rowsum(dO * O), then
+// the log2-domain LSE used by the recompute.
 // stage: -1 all, 0 D preprocess, 1 dK/dV, 2 dQ.
 hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse,

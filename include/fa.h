@@ -115,7 +115,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  * dP = dO V^T, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
  * with dK and dV summed over the query heads that share a kv-head.
  * workspace must hold fa_bwd_workspace_bytes(...) bytes (16-byte aligned; contents
- * ignored on entry). d must be 64, 128 or 256.
+ * ignored on entry; it receives D_i and a log2-scaled copy of lse). d must be 64,
+ * 128 or 256.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -101,7 +101,7 @@ def test_splitkv_validation_and_sizes(lib):
 
 
 def test_bwd_validation_and_workspace(lib):
-    assert lib.fa_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128) == 2 * 32 * 8192 * 4
+    assert lib.fa_bwd_workspace_bytes(2, 32, 8, 8192, 8192, 128) == 2 * (2 * 32 * 8192 * 4)
     assert lib.fa_bwd_workspace_bytes(1, 1, 1, 3, 3, 64) == 256
     ws = lib.fa_bwd_workspace_bytes(1, 2, 1, 8, 8, 128)
     base = [P] * 9
