@@ -73,46 +73,47 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int rows) {
   }
 }
 
-// Row statistic as used by the recompute: log2-domain LSE, +inf for rows that must
-// contribute nothing (padding rows past Nq, and rows that saw no key at all).
-__device__ __forceinline__ float lse2_of(const BwdParams& p, size_t idx, bool valid) {
-  if (!valid) return INFINITY;
-  const float l = p.lse[idx];
-  return l == -INFINITY ? INFINITY : l * kLog2e;
-}
-
-// Asynchronous copy of n consecutive floats (n <= 64; indices clamped to last) into LDS
-// by one wave: one direct global->LDS load of 4 bytes per lane. The LDS destination
-// must have room for 64 floats.
+// Asynchronous copy of 64 consecutive floats (indices clamped to `last`) into LDS by
+// one wave: one direct global->LDS load of 4 bytes per lane.
 __device__ __forceinline__ void vec_load_async(const float* G, int i0, int last, float* lds,
                                                int lane) {
-  const float* src = G + min(i0 + lane, last);
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (FA_LDS void*)lds, 4, 0, 0);
+  lds_dma_dword(G + min(i0 + lane, last), lds);
 }
 
 // ---------------------------------------------------------------------------------
 // 2. dK, dV
 // ---------------------------------------------------------------------------------
-template <int D, int BMQ>
-struct DkdvTile {
-  static constexpr int TILE = TileLayout<D>::elems(BMQ);
-  static constexpr int LPT = BMQ * D / 8 / 256;
-  static_assert(LPT * 256 * 8 == BMQ * D, "tile must split evenly");
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
 };
 
+// One workgroup = 4 waves x 32 keys. Each wave keeps its K and V rows in registers
+// and walks the (query head, 64-query tile) steps that can see its keys. Q/dO tiles
+// and their LSE2/D values are triple buffered in LDS and loaded one step ahead by
+// direct global->LDS copies. A step is software-pipelined in 4 sub-phases per
+// 32-query slice:
+//   S/dP of the slice (d halves 0 and 1), then
+//   dV/dK of the previous slice (its 16-query halves) together with the softmax of
+//   this slice,
+// so the softmax of every slice runs under matrix ops of the wave itself, and only
+// one slice's S/dP accumulators are live at a time. The previous slice of a step's
+// first slice is the last slice of the step before, which is why tiles stay in LDS
+// for two steps. Each sub-phase also reads the LDS operands of the next one.
 template <int D, int BMQ, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) {
-  using T = DkdvTile<D, BMQ>;
   using TL = TileLayout<D>;
-  constexpr int LPT = T::LPT, CPR = D / 8;
-  constexpr int NDC = D / 16, NCB = D / 32, NQS = BMQ / 32;
-  constexpr int BNK = 128;
+  constexpr int TILE = TL::elems(BMQ);
+  constexpr int NDC = D / 16, NCB = D / 32, NQS = BMQ / 32, HD = NDC / 2;
+  constexpr int BNK = 128, NB = 3;
+  constexpr int SV = BMQ < 64 ? 64 : BMQ;  // statistics slots per buffer and kind
+  static_assert(SV % 64 == 0, "statistics rows per step");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * T::TILE];
-  __shared__ __attribute__((aligned(16))) float svec[2 * 2 * BMQ];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NB * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float svec[NB * 2 * SV];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = L % nkb, bkv = L / nkb;
@@ -132,16 +133,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       vreg[dc] = __builtin_bit_cast(bf16x8_t, key < p.Nk ? vs[2 * dc] : z);
     }
   }
+  // nothing may be outstanding in the loops below except the tile copies they issue
+  wait_vmem();
 
+  // Query tiles of every head: [qb0, nqb) can see some key of this workgroup. Tiles
+  // [qb0, qd) touch the causal diagonal and a ragged last tile [qe, nqb) holds rows
+  // past Nq: those steps need masking and run first, in a loop of their own, then the
+  // unmasked tiles [qd, qe).
   int i_start = 0;
   if (CAUSAL) {
     i_start = k0 - p.causal_off;
     if (i_start < 0) i_start = 0;
   }
   const int nqb = (p.Nq + BMQ - 1) / BMQ;
-  const int qb0 = i_start / BMQ;
-  const int per_head = nqb - qb0 > 0 ? nqb - qb0 : 0;
-  const int total = per_head * p.g;
+  const int qb0 = min(i_start / BMQ, nqb);
+  int qd = qb0;
+  if (CAUSAL) {
+    const int lim = k0 + BNK - 1 - p.causal_off;  // first row that sees every key here
+    qd = lim <= 0 ? 0 : (lim + BMQ - 1) / BMQ;
+    qd = max(qb0, min(qd, nqb));
+  }
+  const int qe = p.Nq % BMQ ? nqb - 1 : nqb;
+  const int nu = qe > qd ? qe - qd : 0;        // unmasked tiles per head
+  const int nm = (nqb - qb0) - nu;             // masked tiles per head
+  const int total_m = nm * p.g, total = (nm + nu) * p.g;
+  // step -> (head in the group, first query row)
+  auto step_pos = [&](int s, int& hs, int& i0) {
+    if (s < total_m) {
+      hs = s / nm;
+      const int j = s % nm;
+      i0 = (j < qd - qb0 ? qb0 + j : max(qd, qe) + (j - (qd - qb0))) * BMQ;
+    } else {
+      const int t = s - total_m;
+      hs = t / nu;
+      i0 = (qd + t % nu) * BMQ;
+    }
+  };
 
   f32x16_t dkacc[NCB], dvacc[NCB];
 #pragma unroll
@@ -151,111 +178,198 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   }
   const float c2 = p.scale_log2;
 
-  u32x4_t qpre[LPT], dopre[LPT];
-  float lpre = 0.f, dpre = 0.f;
-  auto gload = [&](int s) {
-    const int h = kvh * p.g + s / per_head;
-    const int i0 = (qb0 + s % per_head) * BMQ;
+  auto qtile = [&](int s) { return smem + (s % NB) * 2 * TILE; };
+  auto stats = [&](int s) { return svec + (s % NB) * 2 * SV; };
+  // Rows past Nq re-read the last row; the softmax of a step that reaches past Nq
+  // zeroes their P and dS.
+  auto issue = [&](int s) {
+    int hs, i0;
+    step_pos(s, hs, i0);
+    const int h = kvh * p.g + hs;
     const size_t hbase = (size_t)(b * p.Hq + h) * p.Nq;
-    // rows past Nq re-read the last row; their LSE is +inf, so P = dS = 0 for them
+    uint16_t* Qs = qtile(s);
+    tile_load_async<D, BMQ, 4>(p.q + hbase * D, i0, p.Nq, Qs, wu, lane);
+    tile_load_async<D, BMQ, 4>(p.dO + hbase * D, i0, p.Nq, Qs + TILE, wu, lane);
+    float* sv = stats(s);
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      const int qi = min(i0 + row, p.Nq - 1);
-      qpre[i] = ((const u32x4_t*)(p.q + (hbase + qi) * D))[col];
-      dopre[i] = ((const u32x4_t*)(p.dO + (hbase + qi) * D))[col];
-    }
-    if (tid < BMQ) {
-      const int qi = i0 + tid;
-      lpre = lse2_of(p, hbase + qi, qi < p.Nq);
-      dpre = qi < p.Nq ? p.dvec[hbase + qi] : 0.f;
+    for (int c = 0; c < SV / 64; ++c) {
+      if (wu == 0) vec_load_async(p.lse2v + hbase, i0 + 64 * c, p.Nq - 1, sv + 64 * c, lane);
+      if (wu == 1) vec_load_async(p.dvec + hbase, i0 + 64 * c, p.Nq - 1, sv + SV + 64 * c, lane);
     }
   };
-  auto lstore = [&](int buf) {
-    uint16_t* Qs = smem + buf * 2 * T::TILE;
-    uint16_t* Os = Qs + T::TILE;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, col = c % CPR;
-      *(FA_LDS u32x4_t*)(Qs + TL::off(row, col * 8)) = qpre[i];
-      *(FA_LDS u32x4_t*)(Os + TL::off(row, col * 8)) = dopre[i];
-    }
-    if (tid < BMQ) {
-      svec[buf * 2 * BMQ + tid] = lpre;
-      svec[buf * 2 * BMQ + BMQ + tid] = dpre;
-    }
-  };
-
-  if (total > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
 
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int wkey0 = k0 + 32 * w;  // first key of this wave
 
-  for (int s = 0; s < total; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < total) gload(s + 1);
-    const uint16_t* Qs = smem + buf * 2 * T::TILE;
-    const uint16_t* Os = Qs + T::TILE;
-    const float* Ls = svec + buf * 2 * BMQ;
-    const float* Ds = Ls + BMQ;
-    const int i0 = (qb0 + s % per_head) * BMQ;
+  // P and dS (bf16, MFMA B-operand layout) of the previous step's last slice
+  bf16x8_t pprev[2], dprev[2];
+  {
+    const u32x4_t z = {0, 0, 0, 0};
+    pprev[0] = pprev[1] = dprev[0] = dprev[1] = __builtin_bit_cast(bf16x8_t, z);
+  }
 
+  // dV += dO^T P, dK += Q^T dS for rows 16kk.. of slice `sl` of the tile at Qs/Os
+  auto rd_g = [&](const uint16_t* Qs, const uint16_t* Os, int sl, int kk, bf16x8_t* ga,
+                  bf16x8_t* gb) {
+    const int rowb = 32 * sl + 16 * kk + tr_row;
 #pragma unroll
-    for (int qs = 0; qs < NQS; ++qs) {
-      const int ib = i0 + 32 * qs;
-      // every (query, key) pair of this wave's 32x32 block is above the diagonal
-      if (CAUSAL && ib + 31 + p.causal_off < wkey0) continue;
-      f32x16_t S = zero16(), dP = zero16();
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int o0 = TL::off(rowb, tr_col + 32 * cb), o1 = TL::off(rowb + 8, tr_col + 32 * cb);
+      ga[cb] = join8(lds_read_tr4(Os + o0), lds_read_tr4(Os + o1));
+      gb[cb] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o1));
+    }
+  };
+  auto mm_g = [&](const bf16x8_t* ga, const bf16x8_t* gb, bf16x8_t pbv, bf16x8_t dbv) {
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const int off = TL::off(32 * qs + l32, 16 * dc + 8 * hi);
-        S = mfma32x32x16(lds_read8(Qs + off), kreg[dc], S);
-        dP = mfma32x32x16(lds_read8(Os + off), vreg[dc], dP);
+    for (int cb = 0; cb < NCB; ++cb) {
+      dvacc[cb] = mfma32x32x16(ga[cb], pbv, dvacc[cb]);
+      dkacc[cb] = mfma32x32x16(gb[cb], dbv, dkacc[cb]);
+    }
+  };
+
+  // MASK: the step touches the causal diagonal or reaches past the last query row.
+  auto step = [&](auto mask_tag, int s, int i0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const uint16_t* Qs = qtile(s);
+    const uint16_t* Os = Qs + TILE;
+    const float* Ls = stats(s);
+    const float* Ds = Ls + SV;
+    const uint16_t* Qp = s > 0 ? qtile(s - 1) : Qs;  // with P = dS = 0 at s = 0
+    const uint16_t* Op = Qp + TILE;
+
+    bf16x8_t sa[2][HD], sb[2][HD];    // Q and dO row operands of an S/dP sub-phase
+    bf16x8_t ga[2][NCB], gb[2][NCB];  // dO^T and Q^T operands of a dV/dK sub-phase
+    f32x4_t lv[2][2], dv[2][2];       // LSE2 and D of the rows of a softmax quarter
+    f32x16_t S, dP;
+    bf16x8_t pc[NQS][2], dsc[NQS][2];
+
+    auto rd_s = [&](int qs, int half) {
+#pragma unroll
+      for (int j = 0; j < HD; ++j) {
+        const int off = TL::off(32 * qs + l32, 16 * (half * HD + j) + 8 * hi);
+        sa[half][j] = lds_read8(Qs + off);
+        sb[half][j] = lds_read8(Os + off);
       }
-      const bool need_mask = CAUSAL && (ib + p.causal_off < wkey0 + 31);
-      uint32_t ppk[8], dspk[8];
+    };
+    auto mm_s = [&](int half) {
+      if (half == 0) {
+        S = zero16();
+        dP = zero16();
+      }
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4_t l4 = *(const FA_LDS f32x4_t*)(Ls + 32 * qs + 8 * rg + 4 * hi);
-        const f32x4_t d4 = *(const FA_LDS f32x4_t*)(Ds + 32 * qs + 8 * rg + 4 * hi);
+      for (int j = 0; j < HD; ++j) {
+        S = mfma32x32x16(sa[half][j], kreg[half * HD + j], S);
+        dP = mfma32x32x16(sb[half][j], vreg[half * HD + j], dP);
+      }
+    };
+    auto rd_ld = [&](int qs, int kk) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int rg = 2 * kk + rr;
+        lv[kk][rr] = *(const FA_LDS f32x4_t*)(Ls + 32 * qs + 8 * rg + 4 * hi);
+        dv[kk][rr] = *(const FA_LDS f32x4_t*)(Ds + 32 * qs + 8 * rg + 4 * hi);
+      }
+    };
+    // accumulator rows 8kk .. 8kk+7 of the slice: P and dS rounded to bf16
+    auto soft = [&](int qs, int kk) {
+      uint32_t pp[4], dd[4];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int rg = 2 * kk + rr;
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
-          float pr = fast_exp2(fmaf(S[r], c2, -l4[e]));
-          if (need_mask && key > ib + 8 * rg + 4 * hi + e + p.causal_off) pr = 0.f;
+          float pr = fast_exp2(fmaf(S[r], c2, -lv[kk][rr][e]));
+          if (MASK) {
+            const int i = i0 + 32 * qs + 8 * rg + 4 * hi + e;
+            if ((CAUSAL && key > i + p.causal_off) || i >= p.Nq) pr = 0.f;
+          }
           pv[e] = pr;
-          dsv[e] = pr * (dP[r] - d4[e]);
+          dsv[e] = pr * (dP[r] - dv[kk][rr][e]);
         }
-        ppk[2 * rg] = pack_bf16x2(pv[0], pv[1]);
-        ppk[2 * rg + 1] = pack_bf16x2(pv[2], pv[3]);
-        dspk[2 * rg] = pack_bf16x2(dsv[0], dsv[1]);
-        dspk[2 * rg + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
+        pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
+        dd[2 * rr] = pack_bf16x2(dsv[0], dsv[1]);
+        dd[2 * rr + 1] = pack_bf16x2(dsv[2], dsv[3]);
       }
+      const u32x4_t pu = {pp[0], pp[1], pp[2], pp[3]};
+      const u32x4_t du = {dd[0], dd[1], dd[2], dd[3]};
+      pc[qs][kk] = __builtin_bit_cast(bf16x8_t, pu);
+      dsc[qs][kk] = __builtin_bit_cast(bf16x8_t, du);
+    };
+    auto interleave = [&]() {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const u32x4_t pu = {ppk[4 * kk], ppk[4 * kk + 1], ppk[4 * kk + 2], ppk[4 * kk + 3]};
-        const u32x4_t du = {dspk[4 * kk], dspk[4 * kk + 1], dspk[4 * kk + 2], dspk[4 * kk + 3]};
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pu);
-        const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
-        const int rowb = 32 * qs + 16 * kk + tr_row;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int o0 = TL::off(rowb, tr_col + 32 * cb), o1 = TL::off(rowb + 8, tr_col + 32 * cb);
-          const bf16x8_t ao = join8(lds_read_tr4(Os + o0), lds_read_tr4(Os + o1));
-          dvacc[cb] = mfma32x32x16(ao, pb, dvacc[cb]);
-          const bf16x8_t aq = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o1));
-          dkacc[cb] = mfma32x32x16(aq, db, dkacc[cb]);
-        }
+      for (int i = 0; i < NDC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix op
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // vector ops
       }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    rd_s(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qs = 0; qs < NQS; ++qs) {
+      // previous slice: the last one of the step before, or qs-1 of this step
+      const uint16_t* Qg = qs == 0 ? Qp : Qs;
+      const uint16_t* Og = qs == 0 ? Op : Os;
+      const int sg = qs == 0 ? NQS - 1 : qs - 1;
+      mm_s(0);
+      rd_s(qs, 1);
+      interleave();
+      mm_s(1);
+      rd_g(Qg, Og, sg, 0, ga[0], gb[0]);
+      rd_ld(qs, 0);
+      interleave();
+      mm_g(ga[0], gb[0], qs == 0 ? pprev[0] : pc[qs - 1][0], qs == 0 ? dprev[0] : dsc[qs - 1][0]);
+      rd_g(Qg, Og, sg, 1, ga[1], gb[1]);
+      rd_ld(qs, 1);
+      soft(qs, 0);
+      interleave();
+      mm_g(ga[1], gb[1], qs == 0 ? pprev[1] : pc[qs - 1][1], qs == 0 ? dprev[1] : dsc[qs - 1][1]);
+      if (qs + 1 < NQS) rd_s(qs + 1, 0);
+      soft(qs, 1);
+      interleave();
     }
-    if (s + 1 < total) lstore(buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      pprev[kk] = pc[NQS - 1][kk];
+      dprev[kk] = dsc[NQS - 1][kk];
+    }
+  };
+
+  if (total > 0) {
+    issue(0);
+    wait_vmem();
+  }
+  __syncthreads();
+
+  int s = 0;
+  for (; s < total_m; ++s) {
+    if (s + 1 < total) issue(s + 1);
+    int hs, i0;
+    step_pos(s, hs, i0);
+    step(BoolC<true>(), s, i0);
+    wait_vmem();
     __syncthreads();
+  }
+  for (; s < total; ++s) {
+    if (s + 1 < total) issue(s + 1);
+    step(BoolC<false>(), s, (qd + (s - total_m) % nu) * BMQ);
+    wait_vmem();
+    __syncthreads();
+  }
+  // dV/dK of the last slice of the last step
+  if (total > 0) {
+    const uint16_t* Qs = qtile(total - 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t ga[NCB], gb[NCB];
+      rd_g(Qs, Qs + TILE, NQS - 1, kk, ga, gb);
+      mm_g(ga, gb, pprev[kk], dprev[kk]);
+    }
   }
 
   if (key < p.Nk) {

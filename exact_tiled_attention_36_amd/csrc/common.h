@@ -114,6 +114,25 @@ struct TileLayout {
   __device__ __forceinline__ static int off(int r, int e) { return row(r) + e; }
 };
 
+// Direct global->LDS copy of one dword per lane (global_load_lds_dword): lane i's 4
+// bytes from `src` land at LDS byte address lds_base + 4*i; `lds_base` must be
+// wave-uniform. Written as inline assembly so that the compiler does not treat the
+// copy as an LDS store of unknown address: it would otherwise wait for every such
+// copy to land before the next LDS read of the wave, i.e. expose the full memory
+// latency of a prefetch that targets a different buffer. Completion is therefore
+// the caller's business: wait_vmem() and a workgroup barrier before the buffer is
+// read. M0 holds the LDS base; one wait state separates its write from the load.
+__device__ __forceinline__ void lds_dma_dword(const void* src, const void* lds_base) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(const FA_LDS void*)lds_base;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(src), "s"(m0v)
+      : "memory", "m0");
+}
+
 // Asynchronous copy of a [ROWS][D] bf16 tile (global rows j0.. of G, clamped to
 // nrows-1) into an LDS tile, by direct global->LDS loads of 4 bytes per lane: each
 // wave instruction fills one contiguous 256-byte piece (128 elements). The NW waves of
@@ -142,8 +161,7 @@ __device__ __forceinline__ void tile_load_async(const uint16_t* G, int j0, int n
       src = G + (size_t)min(j0 + r, nrows - 1) * D + c0 + 2 * lane;
       dst = lds + TileLayout<D>::row(r) + c0;
     }
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (FA_LDS void*)dst, 4, 0, 0);
+    lds_dma_dword(src, dst);
   }
 }
 
