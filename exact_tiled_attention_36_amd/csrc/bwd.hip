@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   const int nm = (nqb - qb0) - nu;             // masked tiles per head
   const int total_m = nm * p.g, total = (nm + nu) * p.g;
   // step -> (head in the group, first query row)
-  auto step_pos = [&](int s, int& hs, int& i0) {
+  auto step_pos = [&](int s, int& hs, int& i0) FA_INLINE {
     if (s < total_m) {
       hs = s / nm;
       const int j = s % nm;
@@ -178,23 +178,88 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   }
   const float c2 = p.scale_log2;
 
-  auto qtile = [&](int s) { return smem + (s % NB) * 2 * TILE; };
-  auto stats = [&](int s) { return svec + (s % NB) * 2 * SV; };
-  // Rows past Nq re-read the last row; the softmax of a step that reaches past Nq
-  // zeroes their P and dS.
-  auto issue = [&](int s) {
+  auto qtile = [&](int s) FA_INLINE { return smem + (s % NB) * 2 * TILE; };
+  auto stats = [&](int s) FA_INLINE { return svec + (s % NB) * 2 * SV; };
+  // Copies of step s: Q and dO tiles (PPW pieces of 256 bytes per wave each) and the
+  // LSE2/D rows. Rows past Nq re-read the last row; the softmax of a step that
+  // reaches past Nq zeroes their P and dS. dma_piece(s, ..., j) issues this wave's
+  // j-th piece, j < 2*PPW, so a step can spread the copies of the next one over its
+  // sub-phases.
+  constexpr int PPW = BMQ * D / 128 / 4;
+  const uint32_t lane_off = 4u * lane;
+  struct StepPos {
+    const uint16_t* q;   // first row of the head's Q / dO
+    const uint16_t* dO;
+    const float* lse2;
+    const float* dvec;
+    int i0;
+  };
+  auto pos_of = [&](int s) FA_INLINE {
     int hs, i0;
     step_pos(s, hs, i0);
-    const int h = kvh * p.g + hs;
-    const size_t hbase = (size_t)(b * p.Hq + h) * p.Nq;
-    uint16_t* Qs = qtile(s);
-    tile_load_async<D, BMQ, 4>(p.q + hbase * D, i0, p.Nq, Qs, wu, lane);
-    tile_load_async<D, BMQ, 4>(p.dO + hbase * D, i0, p.Nq, Qs + TILE, wu, lane);
-    float* sv = stats(s);
+    const size_t hbase = (size_t)(b * p.Hq + kvh * p.g + hs) * p.Nq;
+    StepPos sp;
+    sp.q = p.q + hbase * D;
+    sp.dO = p.dO + hbase * D;
+    sp.lse2 = p.lse2v + hbase;
+    sp.dvec = p.dvec + hbase;
+    sp.i0 = i0;
+    return sp;
+  };
+  auto dma_piece = [&](int s, const StepPos& ps, int j) FA_INLINE {
+    const uint16_t* G = j < PPW ? ps.q : ps.dO;
+    uint16_t* tile = qtile(s) + (j < PPW ? 0 : TILE);
+    const int k = wu + 4 * (j % PPW);  // piece of the tile (uniform)
+    if constexpr (D == 64) {
+      // piece k = rows 2k and 2k+1
+      const int r = 2 * k + (lane >> 5);
+      lds_dma_dword(G + (size_t)min(ps.i0 + r, p.Nq - 1) * D + 2 * (lane & 31),
+                    tile + TL::row(2 * k));
+    } else {
+      constexpr int PPR = D / 128;  // pieces per row
+      const int r = k / PPR, c0 = (k % PPR) * 128;
+      lds_dma_row(G + (size_t)min(ps.i0 + r, p.Nq - 1) * D + c0, lane_off, tile + TL::row(r) + c0);
+    }
+  };
+  // LSE2 rows by waves 0 and 2, D rows by waves 1 and 3 (identical duplicate copies
+  // keep the code free of branches)
+  auto dma_stats = [&](int s, const StepPos& ps) FA_INLINE {
+    float* sv = stats(s) + (wu & 1) * SV;
+    const float* src = (wu & 1) ? ps.dvec : ps.lse2;
 #pragma unroll
-    for (int c = 0; c < SV / 64; ++c) {
-      if (wu == 0) vec_load_async(p.lse2v + hbase, i0 + 64 * c, p.Nq - 1, sv + 64 * c, lane);
-      if (wu == 1) vec_load_async(p.dvec + hbase, i0 + 64 * c, p.Nq - 1, sv + SV + 64 * c, lane);
+    for (int c = 0; c < SV / 64; ++c) vec_load_async(src, ps.i0 + 64 * c, p.Nq - 1, sv + 64 * c, lane);
+  };
+  auto issue_at = [&](int s, const StepPos& ps) FA_INLINE {
+#pragma unroll
+    for (int j = 0; j < 2 * PPW; ++j) dma_piece(s, ps, j);
+    dma_stats(s, ps);
+  };
+  auto issue = [&](int s) FA_INLINE { issue_at(s, pos_of(s)); };
+  // Copies of a tile whose rows all lie below Nq, for D = 128: wave w copies rows
+  // w + 4i (i < 16) of Q and dO. Rows w+16a+4c share one scalar base, the immediate
+  // offset 1024c selects the row (it moves the LDS address by as much), and the LDS
+  // row offset is a per-wave base plus a constant, so a piece costs three scalar
+  // instructions.
+  auto issue_full = [&](int s, const StepPos& ps) FA_INLINE {
+    if constexpr (D == 128 && BMQ == 64) {
+      const uint32_t qb = (uint32_t)(uintptr_t)(const FA_LDS void*)qtile(s) + 320u * wu;
+      const uint16_t* gq = ps.q + (size_t)(ps.i0 + wu) * D;
+      const uint16_t* go = ps.dO + (size_t)(ps.i0 + wu) * D;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t m = qb + 5120u * a;
+        lds_dma_row_imm<0>(gq + 2048 * a, lane_off, m);
+        lds_dma_row_imm<0>(go + 2048 * a, lane_off, m + 2 * TILE);
+        lds_dma_row_imm<1024>(gq + 2048 * a, lane_off, m + 272);
+        lds_dma_row_imm<1024>(go + 2048 * a, lane_off, m + 272 + 2 * TILE);
+        lds_dma_row_imm<2048>(gq + 2048 * a, lane_off, m + 544);
+        lds_dma_row_imm<2048>(go + 2048 * a, lane_off, m + 544 + 2 * TILE);
+        lds_dma_row_imm<3072>(gq + 2048 * a, lane_off, m + 816);
+        lds_dma_row_imm<3072>(go + 2048 * a, lane_off, m + 816 + 2 * TILE);
+      }
+      dma_stats(s, ps);
+    } else {
+      issue_at(s, ps);
     }
   };
 
@@ -210,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
 
   // dV += dO^T P, dK += Q^T dS for rows 16kk.. of slice `sl` of the tile at Qs/Os
   auto rd_g = [&](const uint16_t* Qs, const uint16_t* Os, int sl, int kk, bf16x8_t* ga,
-                  bf16x8_t* gb) {
+                  bf16x8_t* gb) FA_INLINE {
     const int rowb = 32 * sl + 16 * kk + tr_row;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -219,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       gb[cb] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o1));
     }
   };
-  auto mm_g = [&](const bf16x8_t* ga, const bf16x8_t* gb, bf16x8_t pbv, bf16x8_t dbv) {
+  auto mm_g = [&](const bf16x8_t* ga, const bf16x8_t* gb, bf16x8_t pbv, bf16x8_t dbv) FA_INLINE {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       dvacc[cb] = mfma32x32x16(ga[cb], pbv, dvacc[cb]);
@@ -228,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   };
 
   // MASK: the step touches the causal diagonal or reaches past the last query row.
-  auto step = [&](auto mask_tag, int s, int i0) {
+  auto step = [&](auto mask_tag, int s, int i0) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* Qs = qtile(s);
     const uint16_t* Os = Qs + TILE;
@@ -243,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     f32x16_t S, dP;
     bf16x8_t pc[NQS][2], dsc[NQS][2];
 
-    auto rd_s = [&](int qs, int half) {
+    auto rd_s = [&](int qs, int half) FA_INLINE {
 #pragma unroll
       for (int j = 0; j < HD; ++j) {
         const int off = TL::off(32 * qs + l32, 16 * (half * HD + j) + 8 * hi);
@@ -251,7 +316,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
         sb[half][j] = lds_read8(Os + off);
       }
     };
-    auto mm_s = [&](int half) {
+    auto mm_s = [&](int half) FA_INLINE {
       if (half == 0) {
         S = zero16();
         dP = zero16();
@@ -262,7 +327,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
         dP = mfma32x32x16(sb[half][j], vreg[half * HD + j], dP);
       }
     };
-    auto rd_ld = [&](int qs, int kk) {
+    auto rd_ld = [&](int qs, int kk) FA_INLINE {
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int rg = 2 * kk + rr;
@@ -271,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       }
     };
     // accumulator rows 8kk .. 8kk+7 of the slice: P and dS rounded to bf16
-    auto soft = [&](int qs, int kk) {
+    auto soft = [&](int qs, int kk) FA_INLINE {
       uint32_t pp[4], dd[4];
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
@@ -298,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       pc[qs][kk] = __builtin_bit_cast(bf16x8_t, pu);
       dsc[qs][kk] = __builtin_bit_cast(bf16x8_t, du);
     };
-    auto interleave = [&]() {
+    auto interleave = [&]() FA_INLINE {
 #pragma unroll
       for (int i = 0; i < NDC; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix op
@@ -346,6 +411,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   }
   __syncthreads();
 
+  // Step s copies the tiles of step s+1 into buffer (s+1)%3 first (tiles of the
+  // unmasked loop lie wholly below Nq).
   int s = 0;
   for (; s < total_m; ++s) {
     if (s + 1 < total) issue(s + 1);
@@ -356,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     __syncthreads();
   }
   for (; s < total; ++s) {
-    if (s + 1 < total) issue(s + 1);
+    if (s + 1 < total) issue_full(s + 1, pos_of(s + 1));
     step(BoolC<false>(), s, (qd + (s - total_m) % nu) * BMQ);
     wait_vmem();
     __syncthreads();

@@ -30,6 +30,8 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 #define FA_LDS __attribute__((address_space(3)))
+// kernels are written with local lambdas; they must never become real calls
+#define FA_INLINE __attribute__((always_inline))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -131,6 +133,40 @@ __device__ __forceinline__ void lds_dma_dword(const void* src, const void* lds_b
       :
       : "v"(src), "s"(m0v)
       : "memory", "m0");
+}
+
+// Same copy with a wave-uniform global base and a per-lane byte offset (the saddr
+// form): lane i reads gbase + lane_off. With lane_off = 4*lane a wave copies 256
+// contiguous bytes at no vector-ALU cost. No memory clobber: the caller guarantees
+// that nothing reads the destination before its wait_vmem() and barrier, and that no
+// wave still reads it when the copy is issued; volatile asm keeps its order relative
+// to those barriers.
+__device__ __forceinline__ void lds_dma_row(const void* gbase, uint32_t lane_off,
+                                            const void* lds_base) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(const FA_LDS void*)lds_base;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(lane_off), "s"(gbase), "s"(m0v)
+      : "m0");
+}
+
+// Same copy with a scalar base, a per-lane byte offset and an immediate offset IMM
+// that the hardware adds to both addresses: lane i reads gbase + lane_off + IMM and
+// writes LDS byte lds_m0 + IMM + 4*i.
+template <int IMM>
+__device__ __forceinline__ void lds_dma_row_imm(const void* gbase, uint32_t lane_off,
+                                                uint32_t lds_m0) {
+  static_assert(IMM >= 0 && IMM < 4096, "immediate offset range");
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1 offset:%3"
+      :
+      : "v"(lane_off), "s"(gbase), "s"(lds_m0), "i"(IMM)
+      : "m0");
 }
 
 // Asynchronous copy of a [ROWS][D] bf16 tile (global rows j0.. of G, clamped to
