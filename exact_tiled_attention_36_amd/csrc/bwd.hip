@@ -273,15 +273,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     pprev[0] = pprev[1] = dprev[0] = dprev[1] = __builtin_bit_cast(bf16x8_t, z);
   }
 
-  // dV += dO^T P, dK += Q^T dS for rows 16kk.. of slice `sl` of the tile at Qs/Os
-  auto rd_g = [&](const uint16_t* Qs, const uint16_t* Os, int sl, int kk, bf16x8_t* ga,
-                  bf16x8_t* gb) FA_INLINE {
-    const int rowb = 32 * sl + 16 * kk + tr_row;
+  static_assert(TL::shifts_ok(BMQ), "LDS reads add row offsets as constants");
+  // byte address of this lane's transposed reads in a Q tile (dO: + 2*TILE bytes)
+  auto tr_base = [&](const uint16_t* T) FA_INLINE {
+    return opaque(lds_addr(T) + 2 * (TL::row(tr_row) + tr_col));
+  };
+  // dV += dO^T P, dK += Q^T dS for rows 16kk.. of slice `sl` of the tile at tb
+  auto rd_g = [&](uint32_t tb, int sl, int kk, bf16x8_t* ga, bf16x8_t* gb) FA_INLINE {
+    const int R = 32 * sl + 16 * kk;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int o0 = TL::off(rowb, tr_col + 32 * cb), o1 = TL::off(rowb + 8, tr_col + 32 * cb);
-      ga[cb] = join8(lds_read_tr4(Os + o0), lds_read_tr4(Os + o1));
-      gb[cb] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o1));
+      const uint32_t o0 = tb + 2 * (TL::row(R) + 32 * cb), o1 = tb + 2 * (TL::row(R + 8) + 32 * cb);
+      ga[cb] = join8(lds_read_tr4_at(o0 + 2 * TILE), lds_read_tr4_at(o1 + 2 * TILE));
+      gb[cb] = join8(lds_read_tr4_at(o0), lds_read_tr4_at(o1));
     }
   };
   auto mm_g = [&](const bf16x8_t* ga, const bf16x8_t* gb, bf16x8_t pbv, bf16x8_t dbv) FA_INLINE {
@@ -296,11 +300,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   auto step = [&](auto mask_tag, int s, int i0) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* Qs = qtile(s);
-    const uint16_t* Os = Qs + TILE;
-    const float* Ls = stats(s);
-    const float* Ds = Ls + SV;
     const uint16_t* Qp = s > 0 ? qtile(s - 1) : Qs;  // with P = dS = 0 at s = 0
-    const uint16_t* Op = Qp + TILE;
+    // per-lane LDS byte bases of this step's reads (constants are added to them)
+    const uint32_t sbase = opaque(lds_addr(Qs) + 2 * TL::row(l32) + 16 * hi);
+    const uint32_t tcur = tr_base(Qs), tprev = tr_base(Qp);
+    const uint32_t lbase = opaque(lds_addr(stats(s)) + 16 * hi);
 
     bf16x8_t sa[2][HD], sb[2][HD];    // Q and dO row operands of an S/dP sub-phase
     bf16x8_t ga[2][NCB], gb[2][NCB];  // dO^T and Q^T operands of a dV/dK sub-phase
@@ -311,9 +315,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     auto rd_s = [&](int qs, int half) FA_INLINE {
 #pragma unroll
       for (int j = 0; j < HD; ++j) {
-        const int off = TL::off(32 * qs + l32, 16 * (half * HD + j) + 8 * hi);
-        sa[half][j] = lds_read8(Qs + off);
-        sb[half][j] = lds_read8(Os + off);
+        const uint32_t a = sbase + 2 * (TL::row(32 * qs) + 16 * (half * HD + j));
+        sa[half][j] = lds_read8_at(a);
+        sb[half][j] = lds_read8_at(a + 2 * TILE);
       }
     };
     auto mm_s = [&](int half) FA_INLINE {
@@ -331,8 +335,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int rg = 2 * kk + rr;
-        lv[kk][rr] = *(const FA_LDS f32x4_t*)(Ls + 32 * qs + 8 * rg + 4 * hi);
-        dv[kk][rr] = *(const FA_LDS f32x4_t*)(Ds + 32 * qs + 8 * rg + 4 * hi);
+        lv[kk][rr] = lds_read_f4_at(lbase + 4 * (32 * qs + 8 * rg));
+        dv[kk][rr] = lds_read_f4_at(lbase + 4 * (SV + 32 * qs + 8 * rg));
       }
     };
     // accumulator rows 8kk .. 8kk+7 of the slice: P and dS rounded to bf16
@@ -378,18 +382,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       // previous slice: the last one of the step before, or qs-1 of this step
-      const uint16_t* Qg = qs == 0 ? Qp : Qs;
-      const uint16_t* Og = qs == 0 ? Op : Os;
+      const uint32_t tg = qs == 0 ? tprev : tcur;
       const int sg = qs == 0 ? NQS - 1 : qs - 1;
       mm_s(0);
       rd_s(qs, 1);
       interleave();
       mm_s(1);
-      rd_g(Qg, Og, sg, 0, ga[0], gb[0]);
+      rd_g(tg, sg, 0, ga[0], gb[0]);
       rd_ld(qs, 0);
       interleave();
       mm_g(ga[0], gb[0], qs == 0 ? pprev[0] : pc[qs - 1][0], qs == 0 ? dprev[0] : dsc[qs - 1][0]);
-      rd_g(Qg, Og, sg, 1, ga[1], gb[1]);
+      rd_g(tg, sg, 1, ga[1], gb[1]);
       rd_ld(qs, 1);
       soft(qs, 0);
       interleave();
@@ -430,11 +433,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   }
   // dV/dK of the last slice of the last step
   if (total > 0) {
-    const uint16_t* Qs = qtile(total - 1);
+    const uint32_t tb = tr_base(qtile(total - 1));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8_t ga[NCB], gb[NCB];
-      rd_g(Qs, Qs + TILE, NQS - 1, kk, ga, gb);
+      rd_g(tb, NQS - 1, kk, ga, gb);
       mm_g(ga, gb, pprev[kk], dprev[kk]);
     }
   }

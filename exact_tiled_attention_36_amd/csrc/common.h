@@ -67,6 +67,29 @@ __device__ __forceinline__ u32x2_t lds_read_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
+// LDS reads at a byte address. Kernels form a few per-lane base addresses per tile
+// and pass them through opaque(), so the compiler cannot re-associate base and
+// constant parts (it would otherwise keep one register per distinct address and
+// redo the buffer offset for each); the constants then fold into the instructions'
+// 16-bit offset field.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const FA_LDS void*)p;
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ bf16x8_t lds_read8_at(uint32_t a) {
+  return __builtin_bit_cast(bf16x8_t, *(const FA_LDS u32x4_t*)(uintptr_t)a);
+}
+__device__ __forceinline__ u32x2_t lds_read_tr4_at(uint32_t a) {
+  s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4_t*)(uintptr_t)a);
+  return __builtin_bit_cast(u32x2_t, r);
+}
+__device__ __forceinline__ f32x4_t lds_read_f4_at(uint32_t a) {
+  return *(const FA_LDS f32x4_t*)(uintptr_t)a;
+}
+
 __device__ __forceinline__ bf16x8_t join8(u32x2_t lo, u32x2_t hi) {
   u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(bf16x8_t, v);
@@ -102,8 +125,10 @@ struct TileLayout {
   static constexpr int elems(int rows) {
     return D == 64 ? (rows / 16) * 1280 : (rows / 16) * (16 * D + 512);
   }
-  // element offset of row r
-  __device__ __forceinline__ static int row(int r) {
+  // element offset of row r. The pattern repeats every 16 rows (8 for the transposed
+  // reads' 8-row groups), so row(R + r) - row(r) is the same for every lane row r of
+  // the kernels' access patterns; they add it as a constant (checked by shift()).
+  __host__ __device__ static constexpr int row(int r) {
     if constexpr (D == 64) {
       const int m = r >> 1;  // row pair, stored contiguously
       const int a = 4 * (m & 1) + 9 * ((m >> 1) & 3) + 32 * (m >> 3);
@@ -114,6 +139,22 @@ struct TileLayout {
     }
   }
   __device__ __forceinline__ static int off(int r, int e) { return row(r) + e; }
+  // row(R + r) - row(r) for lane rows r < n, or -1 if it depends on r
+  static constexpr int shift(int R, int n) {
+    const int d = row(R) - row(0);
+    for (int r = 0; r < n; ++r)
+      if (row(R + r) - row(r) != d) return -1;
+    return d;
+  }
+  // the kernels' patterns in a tile of `rows` rows: 32-row operand reads at multiples
+  // of 32, transposed reads of 8-row groups at multiples of 8
+  static constexpr bool shifts_ok(int rows) {
+    for (int R = 0; R + 32 <= rows; R += 32)
+      if (shift(R, 32) < 0) return false;
+    for (int R = 0; R + 8 <= rows; R += 8)
+      if (shift(R, 8) < 0) return false;
+    return row(0) == 0;
+  }
 };
 
 // Direct global->LDS copy of one dword per lane (global_load_lds_dword): lane i's 4
