@@ -462,14 +462,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
 // ---------------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------------
+// One workgroup = NW waves x 32 query rows; Q and dO stay in registers, each wave
+// owns its rows' dQ. Key tiles of BN rows (K and V) are triple buffered in LDS and
+// copied two tiles ahead. Step t is one scheduling region:
+//   S, dP of tile t+1 (matrix)       with  dS of tile t (vector),
+//   dQ^T += K_t^T dS^T (matrix)      with  mask of tile t+1 (vector),
+// then the copies' wait and a barrier. S^T and dP^T put one query per lane, so LSE
+// and D are per-lane scalars; dS^T comes out in the B-operand layout of the dQ
+// product, and K^T is read with LDS transpose loads.
 template <int D, int BN, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   using TL = TileLayout<D>;
   constexpr int TILE = TL::elems(BN);
   constexpr int NDC = D / 16, NCB = D / 32, NKB = BN / 32;
   constexpr int BM = 32 * NW;    // query rows per workgroup (one 32-row block per wave)
+  constexpr int NB = 3;
+  static_assert(TL::shifts_ok(BN), "LDS reads add row offsets as constants");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NB * 2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -497,6 +507,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   }
   const float lse2 = qvalid ? p.lse2v[rowidx] : INFINITY;
   const float Dv = qvalid ? p.dvec[rowidx] : 0.f;
+  // nothing may be outstanding in the loops below except the tile copies they issue
+  wait_vmem();
 
   const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
   const uint16_t* Vg = p.v + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
@@ -506,89 +518,137 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
     kend = lim < kend ? lim : kend;
   }
   const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // tiles [0, tfull) are wholly visible to every row of the workgroup
+  int tfull = p.Nk / BN;
+  if (CAUSAL) {
+    const int lim = q0 + p.causal_off + 1;
+    tfull = min(tfull, lim > 0 ? lim / BN : 0);
+  }
+  tfull = min(tfull, ntiles);
 
   f32x16_t dqacc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqacc[cb] = zero16();
   const float c2 = p.scale_log2;
 
-  auto Kb = [&](int i) { return smem + (i & 1) * TILE; };
-  auto Vb = [&](int i) { return smem + (2 + (i & 1)) * TILE; };
+  // buffer t%3 holds the K tile of key tile t, followed by its V tile
+  auto Kb = [&](int t) FA_INLINE { return smem + (t % NB) * 2 * TILE; };
   // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
-  auto load = [&](const uint16_t* G, int t, uint16_t* dst) {
-    tile_load_async<D, BN, NW>(G, t * BN, p.Nk, dst, wu, lane);
+  auto load_tile = [&](int t) FA_INLINE {
+    tile_load_async<D, BN, NW>(Kg, t * BN, p.Nk, Kb(t), wu, lane);
+    tile_load_async<D, BN, NW>(Vg, t * BN, p.Nk, Kb(t) + TILE, wu, lane);
   };
 
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int wlim = w0 + 31 + p.causal_off;  // last key any row of this wave sees
+  const uint32_t srow = 2 * (TL::row(l32) + 8 * hi);
+  const uint32_t trow = 2 * (TL::row(tr_row) + tr_col);
 
-  if (ntiles > 0) {
-    load(Kg, 0, Kb(0));
-    load(Vg, 0, Vb(0));
-    wait_vmem();
-    __syncthreads();
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) {
-      load(Kg, t + 1, Kb(t + 1));
-      load(Vg, t + 1, Vb(t + 1));
+  // S^T = K Q^T and dP^T = V dO^T for key tile t
+  auto compute_sp = [&](f32x16_t (&S)[NKB], f32x16_t (&dP)[NKB], int t) FA_INLINE {
+    const uint32_t kbase = opaque(lds_addr(Kb(t)) + srow);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      S[kb] = zero16();
+      dP[kb] = zero16();
     }
-    const uint16_t* Ks = Kb(t);
-    const uint16_t* Vs = Vb(t);
-    const int j0 = t * BN;
-    // skip tiles that lie wholly above this wave's part of the diagonal
-    if (!CAUSAL || j0 <= wlim) {
-      f32x16_t S[NKB], dP[NKB];
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        S[kb] = zero16();
-        dP[kb] = zero16();
+        const uint32_t a = kbase + 2 * (TL::row(32 * kb) + 16 * dc);
+        S[kb] = mfma32x32x16(lds_read8_at(a), qreg[dc], S[kb]);
+        dP[kb] = mfma32x32x16(lds_read8_at(a + 2 * TILE), doreg[dc], dP[kb]);
       }
+  };
+  // causal / key-tail mask of key tile t: masked scores give P = dS = 0
+  auto mask = [&](f32x16_t (&S)[NKB], int t) FA_INLINE {
+    const int j0 = t * BN;
+    const int lim = CAUSAL ? qrow + p.causal_off : 0x7fffffff;
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int off = TL::off(32 * kb + l32, 16 * dc + 8 * hi);
-          S[kb] = mfma32x32x16(lds_read8(Ks + off), qreg[dc], S[kb]);
-          dP[kb] = mfma32x32x16(lds_read8(Vs + off), doreg[dc], dP[kb]);
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (j >= p.Nk || j > lim) S[kb][r] = -INFINITY;
+      }
+  };
+  // dS = P * (dP - D) with P = exp2(S * scale * log2e - LSE2), bf16 pairs
+  auto dsoft = [&](f32x16_t (&S)[NKB], f32x16_t (&dP)[NKB], uint32_t (&dspk)[NKB][8]) FA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float pr = fast_exp2(fmaf(S[kb][r + e], c2, -lse2));
+          ds2[e] = pr * (dP[kb][r + e] - Dv);
         }
-      const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && (j0 + BN - 1 > w0 + p.causal_off));
-      const int lim = CAUSAL ? qrow + p.causal_off : 0x7fffffff;
-      uint32_t dspk[NKB][8];
+        dspk[kb][r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+      }
+  };
+  // dQ^T += K_t^T dS^T
+  auto dq_mm = [&](const uint32_t (&dspk)[NKB][8], int t) FA_INLINE {
+    const uint32_t tb = opaque(lds_addr(Kb(t)) + trow);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float ds2[2];
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4_t du = {dspk[kb][4 * kk], dspk[kb][4 * kk + 1], dspk[kb][4 * kk + 2], dspk[kb][4 * kk + 3]};
+        const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
+        const int R = 32 * kb + 16 * kk;
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            float pr = fast_exp2(fmaf(S[kb][r + e], c2, -lse2));
-            if (need_mask) {
-              const int j = j0 + 32 * kb + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
-              if (j >= p.Nk || j > lim) pr = 0.f;
-            }
-            ds2[e] = pr * (dP[kb][r + e] - Dv);
-          }
-          dspk[kb][r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+        for (int cb = 0; cb < NCB; ++cb) {
+          const bf16x8_t a = join8(lds_read_tr4_at(tb + 2 * (TL::row(R) + 32 * cb)),
+                                   lds_read_tr4_at(tb + 2 * (TL::row(R + 8) + 32 * cb)));
+          dqacc[cb] = mfma32x32x16(a, db, dqacc[cb]);
         }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4_t du = {dspk[kb][4 * kk], dspk[kb][4 * kk + 1], dspk[kb][4 * kk + 2], dspk[kb][4 * kk + 3]};
-          const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
-          const int kr = 32 * kb + 16 * kk + tr_row;
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const bf16x8_t a = join8(lds_read_tr4(Ks + TL::off(kr, tr_col + 32 * cb)),
-                                     lds_read_tr4(Ks + TL::off(kr + 8, tr_col + 32 * cb)));
-            dqacc[cb] = mfma32x32x16(a, db, dqacc[cb]);
-          }
-        }
+      }
+  };
+
+  // Step t: entering, S/dP of tile t (masked) in (sc, pc), tiles t and t+1 in LDS.
+  // MASK: tile t+1 needs the mask; LAST: there is no tile t+1.
+  f32x16_t sA[NKB], pA[NKB], sB[NKB], pB[NKB];
+  uint32_t dspk[NKB][8];
+  auto step = [&](auto mask_tag, auto last_tag, f32x16_t (&sc)[NKB], f32x16_t (&pc)[NKB],
+                  f32x16_t (&sn)[NKB], f32x16_t (&pn)[NKB], int t) FA_INLINE {
+    constexpr bool MASK = decltype(mask_tag)::value, LAST = decltype(last_tag)::value;
+    if constexpr (!LAST) load_tile(t + 2);  // into the buffer of tile t-1, done with
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) compute_sp(sn, pn, t + 1);
+    dsoft(sc, pc, dspk);
+    dq_mm(dspk, t);
+    if constexpr (!LAST && MASK) mask(sn, t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) {
+      wait_vmem();
+      __syncthreads();
     }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    load_tile(1);
     wait_vmem();
     __syncthreads();
+    compute_sp(sA, pA, 0);
+    if (tfull == 0) mask(sA, 0);
+    int t = 0;
+    for (; t + 2 < tfull && t + 2 < ntiles; t += 2) {
+      step(BoolC<false>(), BoolC<false>(), sA, pA, sB, pB, t);
+      step(BoolC<false>(), BoolC<false>(), sB, pB, sA, pA, t + 1);
+    }
+    for (; t + 2 < ntiles; t += 2) {
+      step(BoolC<true>(), BoolC<false>(), sA, pA, sB, pB, t);
+      step(BoolC<true>(), BoolC<false>(), sB, pB, sA, pA, t + 1);
+    }
+    if (t + 1 < ntiles) {
+      step(BoolC<true>(), BoolC<false>(), sA, pA, sB, pB, t);
+      step(BoolC<false>(), BoolC<true>(), sB, pB, sA, pA, t + 1);
+    } else {
+      step(BoolC<false>(), BoolC<true>(), sA, pA, sB, pB, t);
+    }
   }
 
   if (qvalid) {
@@ -652,8 +712,8 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
   switch (s.d) {
-    case 64: return c ? run<64, 64, 64, 8, true>(p, s.B, stage, st) : run<64, 64, 64, 8, false>(p, s.B, stage, st);
-    case 128: return c ? run<128, 64, 64, 8, true>(p, s.B, stage, st) : run<128, 64, 64, 8, false>(p, s.B, stage, st);
+    case 64: return c ? run<64, 64, 32, 8, true>(p, s.B, stage, st) : run<64, 64, 32, 8, false>(p, s.B, stage, st);
+    case 128: return c ? run<128, 64, 32, 8, true>(p, s.B, stage, st) : run<128, 64, 32, 8, false>(p, s.B, stage, st);
     case 256: return c ? run<256, 32, 32, 4, true>(p, s.B, stage, st) : run<256, 32, 32, 4, false>(p, s.B, stage, st);
     default: return hipErrorInvalidValue;
   }
