@@ -130,7 +130,7 @@ def cpu_baseline(inp, min_seconds=10.0):
                       "S and P materialised"}
 
 
-def extras(torch, fa, iters=10):
+def extras(torch, fa, iters=20):
     """Forward throughput on the other workloads, decode in GB/s (seeded torch.randn)."""
     from exact_tiled_attention_36_amd import synth
     out = {}
@@ -153,7 +153,7 @@ def extras(torch, fa, iters=10):
             call = lambda: fa.fwd_splitkv(q, k, v, causal=causal, out=o, lse=lse, workspace=ws)
         else:
             call = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-        for _ in range(3):
+        for _ in range(5):
             call()
         st = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
