@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   // Query tiles of every head: [qb0, nqb) can see some key of this workgroup. Tiles
   // [qb0, qd) touch the causal diagonal and a ragged last tile [qe, nqb) holds rows
   // past Nq: those steps need masking and run first, in a loop of their own, then the
-  // unmasked tiles [qd, qe).
+  // unmasked tiles [qd, qe) from the top down.
   int i_start = 0;
   if (CAUSAL) {
     i_start = k0 - p.causal_off;
@@ -164,9 +164,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       const int j = s % nm;
       i0 = (j < qd - qb0 ? qb0 + j : max(qd, qe) + (j - (qd - qb0))) * BMQ;
     } else {
+      // unmasked tiles tile-major from the last one down, all heads of the group per
+      // tile: the workgroups of a (batch, kv-head) then read the same Q/dO tiles at
+      // about the same time, so most copies hit in L2
       const int t = s - total_m;
-      hs = t / nu;
-      i0 = (qd + t % nu) * BMQ;
+      hs = t % p.g;
+      i0 = (qe - 1 - t / p.g) * BMQ;
     }
   };
 
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   }
   for (; s < total; ++s) {
     if (s + 1 < total) issue_full(s + 1, pos_of(s + 1));
-    step(BoolC<false>(), s, (qd + (s - total_m) % nu) * BMQ);
+    step(BoolC<false>(), s, (qe - 1 - (s - total_m) / p.g) * BMQ);
     wait_vmem();
     __syncthreads();
   }

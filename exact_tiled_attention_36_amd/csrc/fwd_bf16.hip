@@ -59,10 +59,14 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-template <int D, int BN, int NW, bool CAUSAL>
+// One workgroup = NW waves; wave w owns QS blocks of 32 query rows (BM = 32*QS*NW
+// rows per workgroup). Every K operand and every V^T operand read from LDS feeds the
+// QS blocks, so LDS reads per matrix op fall as 1/QS.
+template <int D, int BN, int NW, int QS, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   using TL = TileLayout<D>;
-  constexpr int BM = 32 * NW;    // query rows per workgroup
+  constexpr int RPW = 32 * QS;   // query rows per wave
+  constexpr int BM = RPW * NW;   // query rows per workgroup
   constexpr int TILE = TL::elems(BN);
   constexpr int NKB = BN / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide chunks of d (reduction of S)
@@ -82,19 +86,20 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.g;
   const int q0 = qb * BM;
-  const int w0 = q0 + 32 * wu;  // first query row of this wave
+  const int w0 = q0 + RPW * wu;  // first query row of this wave
 
   const uint16_t* Qg = p.q + (size_t)(b * p.Hq + h) * p.Nq * D;
   const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
   const uint16_t* Vg = p.v + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
 
-  bf16x8_t qreg[NDC];
-  {
-    const int qrow = w0 + l32;
+  bf16x8_t qreg[QS][NDC];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int qrow = w0 + 32 * qs + l32;
     const int qr = qrow < p.Nq ? qrow : p.Nq - 1;
     const u32x4_t* src = (const u32x4_t*)(Qg + (size_t)qr * D + 8 * hi);
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8_t, src[2 * dc]);
+    for (int dc = 0; dc < NDC; ++dc) qreg[qs][dc] = __builtin_bit_cast(bf16x8_t, src[2 * dc]);
   }
   // nothing may be outstanding in the loops below except the tile copies they issue
   wait_vmem();
@@ -113,10 +118,17 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   }
   tfull = min(tfull, ntiles);
 
-  f32x16_t oacc[NCB];
+  f32x16_t oacc[QS][NCB];
+  float m[QS], lsum[QS], m_use[QS], alpha[QS];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = zero16();
-  float m = -INFINITY, lsum = 0.f, m_use = 0.f;
+  for (int qs = 0; qs < QS; ++qs) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) oacc[qs][cb] = zero16();
+    m[qs] = -INFINITY;
+    lsum[qs] = 0.f;
+    m_use[qs] = 0.f;
+    alpha[qs] = 1.f;
+  }
   const float c2 = p.scale_log2;
 
   auto Kb = [&](int i) FA_INLINE { return smem + (i & 1) * TILE; };
@@ -136,87 +148,110 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   const uint32_t trow = 2 * (TL::row(tr_row) + tr_col);
 
   // S^T = K Q^T for one tile of BN keys
-  auto compute_s = [&](f32x16_t (&sc)[NKB], const uint16_t* Ks) FA_INLINE {
+  auto compute_s = [&](f32x16_t (&sc)[QS][NKB], const uint16_t* Ks) FA_INLINE {
     const uint32_t base = opaque(lds_addr(Ks) + srow);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sc[kb] = zero16();
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sc[qs][kb] = zero16();
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8_t a = lds_read8_at(base + 2 * (TL::row(32 * kb) + 16 * dc));
-        sc[kb] = mfma32x32x16(a, qreg[dc], sc[kb]);
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) sc[qs][kb] = mfma32x32x16(a, qreg[qs][dc], sc[qs][kb]);
       }
   };
 
   // O^T += V^T P^T for one tile
-  auto pv = [&](const uint32_t (&pk)[NKB][8], const uint16_t* Vs) FA_INLINE {
+  auto pv = [&](const uint32_t (&pk)[QS][NKB][8], const uint16_t* Vs) FA_INLINE {
     const uint32_t base = opaque(lds_addr(Vs) + trow);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const u32x4_t bu = {pk[kb][4 * kk], pk[kb][4 * kk + 1], pk[kb][4 * kk + 2], pk[kb][4 * kk + 3]};
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bu);
+        bf16x8_t bop[QS];
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          const u32x4_t bu = {pk[qs][kb][4 * kk], pk[qs][kb][4 * kk + 1], pk[qs][kb][4 * kk + 2],
+                              pk[qs][kb][4 * kk + 3]};
+          bop[qs] = __builtin_bit_cast(bf16x8_t, bu);
+        }
         const int R = 32 * kb + 16 * kk;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const bf16x8_t a = join8(lds_read_tr4_at(base + 2 * (TL::row(R) + 32 * cb)),
                                    lds_read_tr4_at(base + 2 * (TL::row(R + 8) + 32 * cb)));
-          oacc[cb] = mfma32x32x16(a, bop, oacc[cb]);
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs) oacc[qs][cb] = mfma32x32x16(a, bop[qs], oacc[qs][cb]);
         }
       }
   };
 
   // causal / key-tail mask of the scores of tile t
-  auto mask = [&](f32x16_t (&sc)[NKB], int t) FA_INLINE {
+  auto mask = [&](f32x16_t (&sc)[QS][NKB], int t) FA_INLINE {
     const int j0 = t * BN;
-    const int lim = CAUSAL ? w0 + l32 + p.causal_off : 0x7fffffff;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qs = 0; qs < QS; ++qs) {
+      const int lim = CAUSAL ? w0 + 32 * qs + l32 + p.causal_off : 0x7fffffff;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (j >= p.Nk || j > lim) sc[kb][r] = -INFINITY;
-      }
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (j >= p.Nk || j > lim) sc[qs][kb][r] = -INFINITY;
+        }
+    }
   };
 
-  // Row maxima and the lazy-rescale decision; returns whether the base moved (for the
-  // whole wave) and the factor alpha = 2^(m_old - m_new) of each row.
-  auto smax = [&](f32x16_t (&sc)[NKB], float& alpha) FA_INLINE {
-    float mx = -INFINITY;
+  // Row maxima and the lazy-rescale decision; returns whether the base of some block
+  // moved (the rescale branch covers all blocks; unmoved rows have alpha = 1).
+  auto smax = [&](f32x16_t (&sc)[QS][NKB]) FA_INLINE {
+    bool any = false;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qs = 0; qs < QS; ++qs) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = xhalf_max(mx) * c2;
-    const bool move = __any(mx > m + kRescaleSlack);
-    const float m_next = move ? fmaxf(m, mx) : m;
-    m_use = (m_next == -INFINITY) ? 0.f : m_next;
-    alpha = fast_exp2(m - m_use);  // 1 if the base did not move, 0 on first use
-    m = m_next;
-    return move;
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qs][kb][r]);
+      mx = xhalf_max(mx) * c2;
+      const bool move = __any(mx > m[qs] + kRescaleSlack);
+      const float m_next = move ? fmaxf(m[qs], mx) : m[qs];
+      m_use[qs] = (m_next == -INFINITY) ? 0.f : m_next;
+      alpha[qs] = fast_exp2(m[qs] - m_use[qs]);  // 1 if the base did not move, 0 on first use
+      m[qs] = m_next;
+      any |= move;
+    }
+    return any;
   };
   // weights, their row sums and their bf16 packing
-  auto sexp = [&](f32x16_t (&sc)[NKB], uint32_t (&pk)[NKB][8], float alpha) FA_INLINE {
-    float rs = 0.f;
+  auto sexp = [&](f32x16_t (&sc)[QS][NKB], uint32_t (&pk)[QS][NKB][8]) FA_INLINE {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qs = 0; qs < QS; ++qs) {
+      float rs = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(sc[kb][r], c2, -m_use));
-        const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c2, -m_use));
-        rs += p0 + p1;
-        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-      }
-    lsum = fmaf(lsum, alpha, rs);
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(sc[qs][kb][r], c2, -m_use[qs]));
+          const float p1 = fast_exp2(fmaf(sc[qs][kb][r + 1], c2, -m_use[qs]));
+          rs += p0 + p1;
+          pk[qs][kb][r >> 1] = pack_bf16x2(p0, p1);
+        }
+      lsum[qs] = fmaf(lsum[qs], alpha[qs], rs);
+    }
   };
-  auto rescale = [&](float alpha) FA_INLINE {
+  auto rescale = [&]() FA_INLINE {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+    for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[qs][cb][r] *= alpha[qs];
   };
+
   // Step t. Entering: S_t in cur with its mask, row max and rescale decision applied
   // (m, m_use, alpha, move), K_{t+1} in K buffer (t+1)%2 and V_t in V buffer t%2. A
   // pending rescale of O (O holds P_{..t-1} V at the old base) comes first; it is the
@@ -226,25 +261,24 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   //   O += V_t^T P_t (matrix)          with  mask and row max of S_{t+1} (vector),
   // then the copies' wait and a barrier. MASK: tile t+1 needs the mask; LAST: there is
   // no tile t+1.
-  f32x16_t sA[NKB], sB[NKB];
-  uint32_t pk[NKB][8];
+  f32x16_t sA[QS][NKB], sB[QS][NKB];
+  uint32_t pk[QS][NKB][8];
   bool move = false;
-  float alpha = 1.f;
-  auto step = [&](auto mask_tag, auto last_tag, f32x16_t (&cur)[NKB], f32x16_t (&nxt)[NKB],
-                  int t) FA_INLINE {
+  auto step = [&](auto mask_tag, auto last_tag, f32x16_t (&cur)[QS][NKB],
+                  f32x16_t (&nxt)[QS][NKB], int t) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value, LAST = decltype(last_tag)::value;
-    if (move) rescale(alpha);
+    if (move) rescale();
     if constexpr (!LAST) {
       load(Kg, t + 2, Kb(t));
       load(Vg, t + 1, Vb(t + 1));
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!LAST) compute_s(nxt, Kb(t + 1));
-    sexp(cur, pk, alpha);
+    sexp(cur, pk);
     pv(pk, Vb(t));
     if constexpr (!LAST) {
       if constexpr (MASK) mask(nxt, t + 1);
-      move = smax(nxt, alpha);
+      move = smax(nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!LAST) {
@@ -261,7 +295,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     compute_s(sA, Kb(0));
     if (tfull == 0) mask(sA, 0);
-    move = smax(sA, alpha);
+    move = smax(sA);
     __syncthreads();  // K_0's buffer is refilled in step 0
     // S_t in sA at the top of each pair
     int t = 0;
@@ -282,14 +316,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 
   // Epilogue: combine the two half-row sums, normalise once, store O and LSE.
-  {
-    const int qrow = w0 + l32;
-    const float ltot = xhalf_sum(lsum);
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int qrow = w0 + 32 * qs + l32;
+    const float ltot = xhalf_sum(lsum[qs]);
     if (qrow < p.Nq) {
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       if (hi == 0) {
         p.lse[(size_t)(b * p.Hq + h) * p.Nq + qrow] =
-            ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
+            ltot > 0.f ? (m[qs] + log2f(ltot)) * kLn2 : -INFINITY;
       }
       uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + qrow) * D;
 #pragma unroll
@@ -297,21 +332,21 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int c0 = 32 * cb + 8 * rg + 4 * hi;
-          u32x2_t val = {pack_bf16x2(oacc[cb][4 * rg] * inv, oacc[cb][4 * rg + 1] * inv),
-                         pack_bf16x2(oacc[cb][4 * rg + 2] * inv, oacc[cb][4 * rg + 3] * inv)};
+          u32x2_t val = {pack_bf16x2(oacc[qs][cb][4 * rg] * inv, oacc[qs][cb][4 * rg + 1] * inv),
+                         pack_bf16x2(oacc[qs][cb][4 * rg + 2] * inv, oacc[qs][cb][4 * rg + 3] * inv)};
           *(u32x2_t*)(orow + c0) = val;
         }
     }
   }
 }
 
-template <int D, int BN, int NW, bool CAUSAL>
+template <int D, int BN, int NW, int QS, bool CAUSAL>
 hipError_t run(FwdParams p, long long B, hipStream_t st) {
-  constexpr int BM = 32 * NW;
+  constexpr int BM = 32 * NW * QS;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * p.Hq * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, CAUSAL>), dim3((int)nb), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, QS, CAUSAL>), dim3((int)nb), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 
@@ -326,9 +361,15 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
   switch (s.d) {
-    case 64: return c ? run<64, 64, 8, true>(p, s.B, st) : run<64, 64, 8, false>(p, s.B, st);
-    case 128: return c ? run<128, 64, 8, true>(p, s.B, st) : run<128, 64, 8, false>(p, s.B, st);
-    case 256: return c ? run<256, 32, 4, true>(p, s.B, st) : run<256, 32, 4, false>(p, s.B, st);
+#ifndef FWD_CFG128
+#define FWD_CFG128 64, 8, 1
+#endif
+#ifndef FWD_CFG64
+#define FWD_CFG64 64, 8, 1
+#endif
+    case 64: return c ? run<64, FWD_CFG64, true>(p, s.B, st) : run<64, FWD_CFG64, false>(p, s.B, st);
+    case 128: return c ? run<128, FWD_CFG128, true>(p, s.B, st) : run<128, FWD_CFG128, false>(p, s.B, st);
+    case 256: return c ? run<256, 32, 4, 1, true>(p, s.B, st) : run<256, 32, 4, 1, false>(p, s.B, st);
     default: return hipErrorInvalidValue;
   }
 }
