@@ -42,7 +42,8 @@ def to_host64(t) -> np.ndarray:
 
 
 def err_stats(got: np.ndarray, ref: np.ndarray):
-    diff = np.abs(got - ref)
+    with np.errstate(invalid="ignore"):  # -inf - -inf where both sides are -inf
+        diff = np.abs(got - ref)
     finite = np.isfinite(ref)
     if not np.all(finite == np.isfinite(got)):
         return float("inf"), float("inf")

@@ -113,3 +113,22 @@ def test_bwd_validation_and_workspace(lib):
     assert lib.fa_bwd(*base[:4], PU, *base[5:], P, ws, *tail) == -5
     assert lib.fa_bwd(*base, P, ws, 1, 3, 2, 8, 8, 128, 0.1, 1, None) == -3
     assert lib.fa_bwd(*base, P, ws, 1, 2, 1, 8, 8, 80, 0.1, 1, None) == -4
+
+
+def test_bwd_stage_validation(lib):
+    ws = lib.fa_bwd_workspace_bytes(1, 2, 1, 8, 8, 128)
+    args = [P] * 9 + [P, ws, 1, 2, 1, 8, 8, 128, 0.1, 1, None]
+    for stage in (-2, 3, 7):
+        assert lib.fa_bwd_stage(stage, *args) == -11, stage
+    assert lib.fa_bwd_stage(0, *([NULL] + [P] * 8 + [P, ws, 1, 2, 1, 8, 8, 128, 0.1, 1, None])) == -1
+
+
+def test_autograd_refuses_host_tensors():
+    """No host fallback: CPU tensors are rejected before any HIP call."""
+    import torch
+    from exact_tiled_attention_36_amd.autograd import scaled_dot_product_attention
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        scaled_dot_product_attention(q, q, q)
