@@ -174,7 +174,48 @@ def extras(torch, fa, iters=20):
         out[name] = rec
         del q, k, v, o, lse
         torch.cuda.empty_cache()
+    out["v1_vs_v2"] = version_ablation(torch, fa, g)
     return out
+
+
+def version_ablation(torch, fa, g, iters=5):
+    """The first version of the method against the second, on MI355X: the same forward
+    through fa_fwd_variant 0 (deferred normalisation, (batch, head, row-block) grid),
+    1 (renormalise O after every key block, same grid) and 2 (first-version loop
+    order: K/V blocks outer, Q blocks inner, O/m/l through HBM, (batch, head) grid)."""
+    from exact_tiled_attention_36_amd import synth
+    res = {}
+    for name in ("c2_bf16_B2H16N1024d64", "c3a_bf16_causal_B4H32N4096d128"):
+        w = synth.WORKLOADS[name]
+        B, Hq, Hkv, Nq, Nk, d, causal = (w[x] for x in ("B", "Hq", "Hkv", "Nq", "Nk", "d", "causal"))
+        q = torch.randn(B, Hq, Nq, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        k = torch.randn(B, Hkv, Nk, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        v = torch.randn(B, Hkv, Nk, d, device="cuda", dtype=torch.bfloat16, generator=g)
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, Nq, device="cuda", dtype=torch.float32)
+        ws = torch.empty(max(1, fa.load().fa_fwd_variant_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, 2)),
+                         device="cuda", dtype=torch.uint8)
+        fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
+        rec = {}
+        for var in (0, 1, 2):
+            call = lambda: fa.fwd_variant(q, k, v, var, causal=causal, out=o, lse=lse, workspace=ws)
+            for _ in range(3):
+                call()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(iters):
+                call()
+            e1.record(st)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            rec[("deferred", "renorm_every_block", "v1_loop_order")[var]] = {
+                "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+        rec["v2_speedup_over_v1"] = round(rec["v1_loop_order"]["ms"] / rec["deferred"]["ms"], 2)
+        res[name] = rec
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():

@@ -67,6 +67,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_STAGE: return "FA_ERR_STAGE: backward stage must be 0, 1 or 2";
+    case FA_ERR_VARIANT: return "FA_ERR_VARIANT: forward variant must be 0, 1 or 2";
     default: return "unknown fa status code";
   }
 }
@@ -181,6 +182,37 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
   if (stage < 0 || stage > 2) return FA_ERR_STAGE;
   return bwd_common(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
                     Nq, Nk, d, scale, causal, stage, stream);
+}
+
+size_t fa_fwd_variant_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                      int variant) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  if (variant != 2) return 0;
+  return align256(fa::fwd_v1_workspace_floats(shape(B, Hq, Hkv, Nq, Nk, d, 1.f, 0)) *
+                  sizeof(float));
+}
+
+int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                   int Nk, int d, float scale, int causal, int variant, void* stream) {
+  if (variant < 0 || variant > 2) return FA_ERR_VARIANT;
+  if (variant == 0) return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream);
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const fa::AttnShape s = shape(B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (variant == 1)
+    return launch_status(fa::launch_fwd_bf16_renorm((const uint16_t*)q, (const uint16_t*)k,
+                                                    (const uint16_t*)v, (uint16_t*)o, lse, s,
+                                                    (hipStream_t)stream));
+  const size_t need = fa_fwd_variant_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, variant);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  return launch_status(fa::launch_fwd_v1((const uint16_t*)q, (const uint16_t*)k,
+                                         (const uint16_t*)v, (uint16_t*)o, lse,
+                                         (float*)workspace, s, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -62,7 +62,13 @@ struct BoolC {
 // One workgroup = NW waves; wave w owns QS blocks of 32 query rows (BM = 32*QS*NW
 // rows per workgroup). Every K operand and every V^T operand read from LDS feeds the
 // QS blocks, so LDS reads per matrix op fall as 1/QS.
-template <int D, int BN, int NW, int QS, bool CAUSAL>
+// RENORM (ablation only, not the production path): the FlashAttention-1 update of
+// "FlashAttention" (ruizhehou.github.io) §二.2, which keeps O normalised after every
+// key block: the running max is exact (no slack), and each tile scales O by
+// alpha * l_old / l_new and P by 1 / l_new before the product, so the epilogue does
+// not divide. Same grid and pipeline as the deferred (§四.1) form, so timing the two
+// isolates the cost of renormalising every block.
+template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   constexpr int RPW = 32 * QS;   // query rows per wave
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qs][kb][r]);
       mx = xhalf_max(mx) * c2;
-      const bool move = __any(mx > m[qs] + kRescaleSlack);
+      const bool move = __any(mx > m[qs] + (RENORM ? 0.f : kRescaleSlack));
       const float m_next = move ? fmaxf(m[qs], mx) : m[qs];
       m_use[qs] = (m_next == -INFINITY) ? 0.f : m_next;
       alpha[qs] = fast_exp2(m[qs] - m_use[qs]);  // 1 if the base did not move, 0 on first use
@@ -231,16 +237,42 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       float rs = 0.f;
+      if constexpr (!RENORM) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(sc[qs][kb][r], c2, -m_use[qs]));
-          const float p1 = fast_exp2(fmaf(sc[qs][kb][r + 1], c2, -m_use[qs]));
-          rs += p0 + p1;
-          pk[qs][kb][r >> 1] = pack_bf16x2(p0, p1);
-        }
-      lsum[qs] = fmaf(lsum[qs], alpha[qs], rs);
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(sc[qs][kb][r], c2, -m_use[qs]));
+            const float p1 = fast_exp2(fmaf(sc[qs][kb][r + 1], c2, -m_use[qs]));
+            rs += p0 + p1;
+            pk[qs][kb][r >> 1] = pack_bf16x2(p0, p1);
+          }
+        lsum[qs] = fmaf(lsum[qs], alpha[qs], rs);
+      } else {
+        float pv[NKB][16];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pv[kb][r] = fast_exp2(fmaf(sc[qs][kb][r], c2, -m_use[qs]));
+            rs += pv[kb][r];
+          }
+        const float l_old = lsum[qs];
+        lsum[qs] = fmaf(l_old, alpha[qs], rs);
+        // O <- O * alpha * l_old / l_new, P <- P / l_new (whole-row sums)
+        const float lt_old = xhalf_sum(l_old), lt_new = xhalf_sum(lsum[qs]);
+        const float pscale = lt_new > 0.f ? 1.f / lt_new : 0.f;
+        const float oscale = alpha[qs] * lt_old * pscale;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qs][cb][r] *= oscale;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            pk[qs][kb][r >> 1] = pack_bf16x2(pv[kb][r] * pscale, pv[kb][r + 1] * pscale);
+      }
     }
   };
   auto rescale = [&]() FA_INLINE {
@@ -267,7 +299,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   auto step = [&](auto mask_tag, auto last_tag, f32x16_t (&cur)[QS][NKB],
                   f32x16_t (&nxt)[QS][NKB], int t) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value, LAST = decltype(last_tag)::value;
-    if (move) rescale();
+    if (!RENORM && move) rescale();
     if constexpr (!LAST) {
       load(Kg, t + 2, Kb(t));
       load(Vg, t + 1, Vb(t + 1));
@@ -321,7 +353,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
     const int qrow = w0 + 32 * qs + l32;
     const float ltot = xhalf_sum(lsum[qs]);
     if (qrow < p.Nq) {
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      const float inv = RENORM ? 1.f : (ltot > 0.f ? 1.f / ltot : 0.f);
       if (hi == 0) {
         p.lse[(size_t)(b * p.Hq + h) * p.Nq + qrow] =
             ltot > 0.f ? (m[qs] + log2f(ltot)) * kLn2 : -INFINITY;
@@ -340,13 +372,13 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BN, int NW, int QS, bool CAUSAL>
+template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false>
 hipError_t run(FwdParams p, long long B, hipStream_t st) {
   constexpr int BM = 32 * NW * QS;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * p.Hq * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, QS, CAUSAL>), dim3((int)nb), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, QS, CAUSAL, RENORM>), dim3((int)nb), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 
@@ -370,6 +402,22 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
     case 64: return c ? run<64, FWD_CFG64, true>(p, s.B, st) : run<64, FWD_CFG64, false>(p, s.B, st);
     case 128: return c ? run<128, FWD_CFG128, true>(p, s.B, st) : run<128, FWD_CFG128, false>(p, s.B, st);
     case 256: return c ? run<256, 32, 4, 1, true>(p, s.B, st) : run<256, 32, 4, 1, false>(p, s.B, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+
+hipError_t launch_fwd_bf16_renorm(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  uint16_t* o, float* lse, const AttnShape& s, hipStream_t st) {
+  FwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.Hq = s.Hq; p.Hkv = s.Hkv; p.Nq = s.Nq; p.Nk = s.Nk; p.g = s.Hq / s.Hkv;
+  p.causal_off = s.Nk - s.Nq;
+  p.scale_log2 = s.scale * kLog2e;
+  const bool c = s.causal != 0;
+  switch (s.d) {
+    case 64: return c ? run<64, 64, 8, 1, true, true>(p, s.B, st) : run<64, 64, 8, 1, false, true>(p, s.B, st);
+    case 128: return c ? run<128, 64, 8, 1, true, true>(p, s.B, st) : run<128, 64, 8, 1, false, true>(p, s.B, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,6 +16,16 @@ struct AttnShape {
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            uint16_t* o, float* lse, const AttnShape& s, hipStream_t st);
 
+// Ablation forwards (d in {64,128}), same outputs as launch_fwd_bf16:
+// renorm: production grid, O renormalised after every key block;
+// v1: K/V-block outer loop, Q-block inner loop, one workgroup per (batch, head), with
+// an fp32 workspace of fwd_v1_workspace_floats(s) floats.
+hipError_t launch_fwd_bf16_renorm(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  uint16_t* o, float* lse, const AttnShape& s, hipStream_t st);
+size_t fwd_v1_workspace_floats(const AttnShape& s);
+hipError_t launch_fwd_v1(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                         float* lse, float* ws, const AttnShape& s, hipStream_t st);
+
 // Forward, fp32 in/out (d % 4 == 0, d <= 256).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
                           float* lse, const AttnShape& s, hipStream_t st);

@@ -36,6 +36,9 @@ _SIGNATURES = {
     "fa_bwd": (_c_int, [_vp] * 10 + [_c_size] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
     "fa_bwd_stage": (_c_int, [_c_int] + [_vp] * 10 + [_c_size] + [_c_int] * 6
                      + [_c_float, _c_int, _vp]),
+    "fa_fwd_variant_workspace_bytes": (_c_size, [_c_int] * 7),
+    "fa_fwd_variant": (_c_int, [_vp] * 6 + [_c_size] + [_c_int] * 6
+                       + [_c_float, _c_int, _c_int, _vp]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -121,6 +124,36 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
     st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)), _stream(q.device))
     _check(name, st)
+    return out, lse
+
+
+FWD_VARIANTS = {"deferred": 0, "renorm_every_block": 1, "v1_loop_order": 2}
+
+
+def fwd_variant(q, k, v, variant, causal: bool = False, scale: Optional[float] = None,
+                out=None, lse=None, workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O and LSE (bf16) through one of the comparison variants of fa_fwd_variant:
+    0 / "deferred" (fa_fwd), 1 / "renorm_every_block", 2 / "v1_loop_order"."""
+    import torch
+    lib = load()
+    var = FWD_VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("fwd_variant takes bfloat16 inputs")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    nbytes = lib.fa_fwd_variant_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, var)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wlen = workspace.numel() if workspace is not None else 0
+    st = lib.fa_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), wptr, wlen, B, Hq, Hkv, Nq, Nk, d, sc,
+                            int(bool(causal)), var, _stream(q.device))
+    _check("fa_fwd_variant", st)
     return out, lse
 
 

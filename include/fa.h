@@ -59,7 +59,8 @@ enum {
   FA_ERR_TOO_LARGE = -8,  /* an index would overflow 32/64-bit addressing limits */
   FA_ERR_SPLITS = -9,     /* num_splits out of range                             */
   FA_ERR_SCALE = -10,     /* scale is not a finite number > 0                    */
-  FA_ERR_STAGE = -11      /* fa_bwd_stage: stage not in {0, 1, 2}                */
+  FA_ERR_STAGE = -11,     /* fa_bwd_stage: stage not in {0, 1, 2}                */
+  FA_ERR_VARIANT = -12    /* fa_fwd_variant: variant not in {0, 1, 2}            */
 };
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -136,6 +137,31 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const void* dO, const float* lse, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
                  int Nk, int d, float scale, int causal, void* stream);
+
+/*
+ * Forward-pass variants for the comparison of the first and second versions of the
+ * method ("FlashAttention" (ruizhehou.github.io): §二.2 and §三 for the first, §四.1 and
+ * §四.2 for what the second changes). All three return the same O (bf16) and lse
+ * (float32) as fa_fwd, up to rounding; only how the work is organised differs:
+ *   variant 0: fa_fwd itself (deferred normalisation, grid over (batch, head, row
+ *              block)); workspace unused, may be NULL.
+ *   variant 1: fa_fwd's grid and pipeline, but O renormalised after every key block
+ *              (the first version's update, §二.2): isolates the cost of the extra
+ *              rescaling the second version removes. workspace unused.
+ *   variant 2: the first version's loop order: one workgroup per (batch, head), K/V
+ *              blocks in the outer loop, 128-row Q blocks in the inner loop, O, m and
+ *              l read from and written back to `workspace` (fp32) for every pair of
+ *              blocks, then a final pass writes o and lse.
+ * Variants 1 and 2 take d in {64, 128} (FA_ERR_HEAD_DIM otherwise). Other arguments,
+ * layouts, alignment and errors as fa_fwd; workspace must hold
+ * fa_fwd_variant_workspace_bytes(...) bytes, 16-byte aligned (FA_ERR_WORKSPACE), and
+ * its contents need no initialisation. Unknown variant: FA_ERR_VARIANT.
+ */
+size_t fa_fwd_variant_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                      int variant);
+int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                   int Nk, int d, float scale, int causal, int variant, void* stream);
 
 #ifdef __cplusplus
 }

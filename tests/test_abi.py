@@ -132,3 +132,20 @@ def test_autograd_refuses_host_tensors():
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         scaled_dot_product_attention(q, q, q)
+
+
+def test_fwd_variant_validation(lib):
+    args = [P, P, P, P, P, P, 1 << 30, 1, 2, 1, 8, 8, 128, 0.1, 1]
+    assert lib.fa_fwd_variant(*args, 3, None) == -12
+    assert lib.fa_fwd_variant(*args, -1, None) == -12
+    d256 = [P, P, P, P, P, P, 1 << 30, 1, 2, 1, 8, 8, 256, 0.1, 1]
+    assert lib.fa_fwd_variant(*d256, 1, None) == -4
+    assert lib.fa_fwd_variant(*d256, 2, None) == -4
+    ws = lib.fa_fwd_variant_workspace_bytes(1, 2, 1, 8, 8, 128, 2)
+    assert ws >= 2 * 128 * 128 * 4                     # one 128-row block of O per head
+    assert lib.fa_fwd_variant_workspace_bytes(1, 2, 1, 8, 8, 128, 1) == 0
+    small = [P, P, P, P, P, P, ws - 1, 1, 2, 1, 8, 8, 128, 0.1, 1]
+    assert lib.fa_fwd_variant(*small, 2, None) == -6
+    nows = [P, P, P, P, P, NULL, ws, 1, 2, 1, 8, 8, 128, 0.1, 1]
+    assert lib.fa_fwd_variant(*nows, 2, None) == -6
+    assert lib.fa_fwd_variant(NULL, *args[1:], 1, None) == -1
