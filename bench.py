@@ -178,12 +178,16 @@ def extras(torch, fa, iters=20):
     return out
 
 
-def version_ablation(torch, fa, g, iters=5):
+def version_ablation(torch, fa, g, iters=5, reps=5):
     """The first version of the method against the second, on MI355X: the same forward
     through fa_fwd_variant 0 (deferred normalisation, (batch, head, row-block) grid),
-    1 (renormalise O after every key block, same grid) and 2 (first-version loop
-    order: K/V blocks outer, Q blocks inner, O/m/l through HBM, (batch, head) grid)."""
+    1 (renormalise O after every key block, same grid), 2 (first-version loop
+    order: K/V blocks outer, Q blocks inner, O/m/l through HBM, (batch, head) grid) and
+    3 (fa_fwd with every eighth exponential computed by a polynomial). The variants are
+    timed in turn, reps times over, and the median of each is reported."""
+    import statistics
     from exact_tiled_attention_36_amd import synth
+    names = ("deferred", "renorm_every_block", "v1_loop_order", "poly_exp_1_in_8")
     res = {}
     for name in ("c2_bf16_B2H16N1024d64", "c3a_bf16_causal_B4H32N4096d128"):
         w = synth.WORKLOADS[name]
@@ -196,21 +200,24 @@ def version_ablation(torch, fa, g, iters=5):
         ws = torch.empty(max(1, fa.load().fa_fwd_variant_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, 2)),
                          device="cuda", dtype=torch.uint8)
         fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
+        times = {var: [] for var in range(4)}
+        st = torch.cuda.current_stream()
+        for _ in range(reps):
+            for var in range(4):
+                call = lambda: fa.fwd_variant(q, k, v, var, causal=causal, out=o, lse=lse, workspace=ws)
+                for _ in range(2):
+                    call()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                for _ in range(iters):
+                    call()
+                e1.record(st)
+                torch.cuda.synchronize()
+                times[var].append(e0.elapsed_time(e1) / iters)
         rec = {}
-        for var in (0, 1, 2):
-            call = lambda: fa.fwd_variant(q, k, v, var, causal=causal, out=o, lse=lse, workspace=ws)
-            for _ in range(3):
-                call()
-            st = torch.cuda.current_stream()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(iters):
-                call()
-            e1.record(st)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / iters
-            rec[("deferred", "renorm_every_block", "v1_loop_order")[var]] = {
-                "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+        for var in range(4):
+            ms = statistics.median(times[var])
+            rec[names[var]] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
         rec["v2_speedup_over_v1"] = round(rec["v1_loop_order"]["ms"] / rec["deferred"]["ms"], 2)
         res[name] = rec
         del q, k, v, o, lse, ws

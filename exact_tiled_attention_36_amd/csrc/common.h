@@ -112,6 +112,21 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the FMA units instead of the transcendental unit: x = n + f with n = rint(x),
+// |f| <= 1/2 (Cody-Waite style reduction), 2^f by a degree-3 polynomial with minimax
+// relative error 8.4e-5 on [-1/2, 1/2] (coefficients fitted by csrc/fit_exp2_poly.py),
+// scaled by 2^n with ldexp. x is clamped at -200 first, so -inf (a masked score) gives
+// exactly 0 and never a NaN.
+__device__ __forceinline__ float poly_exp2(float x) {
+  x = fmaxf(x, -200.f);
+  const float n = __builtin_rintf(x);
+  const float f = x - n;
+  float p = fmaf(0.055212993f, f, 0.24271414f);
+  p = fmaf(p, f, 0.69326216f);
+  p = fmaf(p, f, 0.99991959f);
+  return __builtin_amdgcn_ldexpf(p, (int)n);
+}
+
 // LDS layout of a [rows][D] bf16 tile (rows a multiple of 16). Every tile is read
 // two ways: 16-byte row reads (lanes 0..31 read 32 different rows at one column
 // chunk: MFMA A operands) and transposed reads (each 16-lane group reads 4

@@ -67,7 +67,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_STAGE: return "FA_ERR_STAGE: backward stage must be 0, 1 or 2";
-    case FA_ERR_VARIANT: return "FA_ERR_VARIANT: forward variant must be 0, 1 or 2";
+    case FA_ERR_VARIANT: return "FA_ERR_VARIANT: forward variant must be 0, 1, 2 or 3";
     default: return "unknown fa status code";
   }
 }
@@ -195,7 +195,7 @@ size_t fa_fwd_variant_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, in
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
                    int Nk, int d, float scale, int causal, int variant, void* stream) {
-  if (variant < 0 || variant > 2) return FA_ERR_VARIANT;
+  if (variant < 0 || variant > 3) return FA_ERR_VARIANT;
   if (variant == 0) return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream);
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
@@ -204,10 +204,10 @@ int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   const fa::AttnShape s = shape(B, Hq, Hkv, Nq, Nk, d, scale, causal);
-  if (variant == 1)
-    return launch_status(fa::launch_fwd_bf16_renorm((const uint16_t*)q, (const uint16_t*)k,
-                                                    (const uint16_t*)v, (uint16_t*)o, lse, s,
-                                                    (hipStream_t)stream));
+  if (variant == 1 || variant == 3)
+    return launch_status(fa::launch_fwd_bf16_variant((const uint16_t*)q, (const uint16_t*)k,
+                                                     (const uint16_t*)v, (uint16_t*)o, lse, s,
+                                                     variant, (hipStream_t)stream));
   const size_t need = fa_fwd_variant_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, variant);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   return launch_status(fa::launch_fwd_v1((const uint16_t*)q, (const uint16_t*)k,

@@ -68,7 +68,10 @@ struct BoolC {
 // alpha * l_old / l_new and P by 1 / l_new before the product, so the epilogue does
 // not divide. Same grid and pipeline as the deferred (§四.1) form, so timing the two
 // isolates the cost of renormalising every block.
-template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false>
+// POLY (ablation only): every eighth weight 2^x is computed by poly_exp2 on the FMA
+// units instead of v_exp_f32, the partial software exponential that the wiki lists
+// for FlashAttention-4 (核心技術), to move work off the transcendental unit.
+template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false, bool POLY = false>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   constexpr int RPW = 32 * QS;   // query rows per wave
@@ -242,8 +245,10 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(sc[qs][kb][r], c2, -m_use[qs]));
-            const float p1 = fast_exp2(fmaf(sc[qs][kb][r + 1], c2, -m_use[qs]));
+            const float x0 = fmaf(sc[qs][kb][r], c2, -m_use[qs]);
+            const float x1 = fmaf(sc[qs][kb][r + 1], c2, -m_use[qs]);
+            const float p0 = fast_exp2(x0);
+            const float p1 = (POLY && (r + 1) % 8 == 7) ? poly_exp2(x1) : fast_exp2(x1);
             rs += p0 + p1;
             pk[qs][kb][r >> 1] = pack_bf16x2(p0, p1);
           }
@@ -372,13 +377,13 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false>
+template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false, bool POLY = false>
 hipError_t run(FwdParams p, long long B, hipStream_t st) {
   constexpr int BM = 32 * NW * QS;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * p.Hq * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, QS, CAUSAL, RENORM>), dim3((int)nb), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, QS, CAUSAL, RENORM, POLY>), dim3((int)nb), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 
@@ -407,19 +412,30 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 }
 
 
-hipError_t launch_fwd_bf16_renorm(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                  uint16_t* o, float* lse, const AttnShape& s, hipStream_t st) {
+hipError_t launch_fwd_bf16_variant(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* o, float* lse, const AttnShape& s, int variant,
+                                   hipStream_t st) {
   FwdParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.Hq = s.Hq; p.Hkv = s.Hkv; p.Nq = s.Nq; p.Nk = s.Nk; p.g = s.Hq / s.Hkv;
   p.causal_off = s.Nk - s.Nq;
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
-  switch (s.d) {
-    case 64: return c ? run<64, 64, 8, 1, true, true>(p, s.B, st) : run<64, 64, 8, 1, false, true>(p, s.B, st);
-    case 128: return c ? run<128, 64, 8, 1, true, true>(p, s.B, st) : run<128, 64, 8, 1, false, true>(p, s.B, st);
-    default: return hipErrorInvalidValue;
+  if (variant == 1) {
+    switch (s.d) {
+      case 64: return c ? run<64, 64, 8, 1, true, true>(p, s.B, st) : run<64, 64, 8, 1, false, true>(p, s.B, st);
+      case 128: return c ? run<128, 64, 8, 1, true, true>(p, s.B, st) : run<128, 64, 8, 1, false, true>(p, s.B, st);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (variant == 3) {
+    switch (s.d) {
+      case 64: return c ? run<64, 64, 8, 1, true, false, true>(p, s.B, st) : run<64, 64, 8, 1, false, false, true>(p, s.B, st);
+      case 128: return c ? run<128, 64, 8, 1, true, false, true>(p, s.B, st) : run<128, 64, 8, 1, false, false, true>(p, s.B, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -17,11 +17,13 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            uint16_t* o, float* lse, const AttnShape& s, hipStream_t st);
 
 // Ablation forwards (d in {64,128}), same outputs as launch_fwd_bf16:
-// renorm: production grid, O renormalised after every key block;
+// variant 1: production grid, O renormalised after every key block;
+// variant 3: production kernel with every eighth exponential computed in software;
 // v1: K/V-block outer loop, Q-block inner loop, one workgroup per (batch, head), with
 // an fp32 workspace of fwd_v1_workspace_floats(s) floats.
-hipError_t launch_fwd_bf16_renorm(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                  uint16_t* o, float* lse, const AttnShape& s, hipStream_t st);
+hipError_t launch_fwd_bf16_variant(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* o, float* lse, const AttnShape& s, int variant,
+                                   hipStream_t st);
 size_t fwd_v1_workspace_floats(const AttnShape& s);
 hipError_t launch_fwd_v1(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                          float* lse, float* ws, const AttnShape& s, hipStream_t st);

@@ -127,13 +127,15 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
     return out, lse
 
 
-FWD_VARIANTS = {"deferred": 0, "renorm_every_block": 1, "v1_loop_order": 2}
+FWD_VARIANTS = {"deferred": 0, "renorm_every_block": 1, "v1_loop_order": 2,
+                "poly_exp_1_in_8": 3}
 
 
 def fwd_variant(q, k, v, variant, causal: bool = False, scale: Optional[float] = None,
                 out=None, lse=None, workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """O and LSE (bf16) through one of the comparison variants of fa_fwd_variant:
-    0 / "deferred" (fa_fwd), 1 / "renorm_every_block", 2 / "v1_loop_order"."""
+    0 / "deferred" (fa_fwd), 1 / "renorm_every_block", 2 / "v1_loop_order",
+    3 / "poly_exp_1_in_8"."""
     import torch
     lib = load()
     var = FWD_VARIANTS[variant] if isinstance(variant, str) else int(variant)

@@ -60,7 +60,7 @@ enum {
   FA_ERR_SPLITS = -9,     /* num_splits out of range                             */
   FA_ERR_SCALE = -10,     /* scale is not a finite number > 0                    */
   FA_ERR_STAGE = -11,     /* fa_bwd_stage: stage not in {0, 1, 2}                */
-  FA_ERR_VARIANT = -12    /* fa_fwd_variant: variant not in {0, 1, 2}            */
+  FA_ERR_VARIANT = -12    /* fa_fwd_variant: variant not in {0, 1, 2, 3}         */
 };
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -152,7 +152,12 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
  *              blocks in the outer loop, 128-row Q blocks in the inner loop, O, m and
  *              l read from and written back to `workspace` (fp32) for every pair of
  *              blocks, then a final pass writes o and lse.
- * Variants 1 and 2 take d in {64, 128} (FA_ERR_HEAD_DIM otherwise). Other arguments,
+ *   variant 3: fa_fwd with every eighth exponential computed by a polynomial on the
+ *              FMA units (range reduction to [-1/2, 1/2], degree-3 minimax, relative
+ *              error < 1e-4) instead of the transcendental unit: the partial software
+ *              exponential the wiki names for the fourth version ("FlashAttention"
+ *              (newton.com.tw), 核心技術). workspace unused.
+ * Variants 1 to 3 take d in {64, 128} (FA_ERR_HEAD_DIM otherwise). Other arguments,
  * layouts, alignment and errors as fa_fwd; workspace must hold
  * fa_fwd_variant_workspace_bytes(...) bytes, 16-byte aligned (FA_ERR_WORKSPACE), and
  * its contents need no initialisation. Unknown variant: FA_ERR_VARIANT.

@@ -136,7 +136,7 @@ def test_autograd_refuses_host_tensors():
 
 def test_fwd_variant_validation(lib):
     args = [P, P, P, P, P, P, 1 << 30, 1, 2, 1, 8, 8, 128, 0.1, 1]
-    assert lib.fa_fwd_variant(*args, 3, None) == -12
+    assert lib.fa_fwd_variant(*args, 4, None) == -12
     assert lib.fa_fwd_variant(*args, -1, None) == -12
     d256 = [P, P, P, P, P, P, 1 << 30, 1, 2, 1, 8, 8, 256, 0.1, 1]
     assert lib.fa_fwd_variant(*d256, 1, None) == -4

@@ -21,7 +21,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("variant", ["renorm_every_block", "v1_loop_order"])
+@pytest.mark.parametrize("variant", ["renorm_every_block", "v1_loop_order", "poly_exp_1_in_8"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_variant_matches_oracle(gpu_lib, shape, variant):
     import torch
