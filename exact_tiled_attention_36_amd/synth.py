@@ -8,7 +8,11 @@ This module holds no attention arithmetic. It only draws numbers and stores them
   the generator hands out the raw 16-bit patterns so that the GPU buffers and the
   oracle's float64 copies are built from exactly the same bits;
 * an optional power-of-two multiplier on Q (exact in binary floating point) drives
-  large logits through the online-softmax rescale.
+  large logits through the online-softmax rescale;
+* FP8 inputs (``make_fp8_inputs``) are E4M3 codes with one float32 scale per tensor:
+  either the same normal draws scaled so that each tensor's largest magnitude maps to
+  E4M3's largest finite value 448 and rounded to nearest even ("gauss"), or sparse
+  sign patterns whose scores are small integers ("signs", see that function).
 
 The pages' own accuracy harness (FlashAttention1 pseudo-implementation article on
 gitcode.csdn.net, §三, its test block) draws ``torch.randn`` Q, K, V; these inputs
@@ -145,3 +149,109 @@ def workload(name: str, **over) -> AttnInputs:
     kw = dict(WORKLOADS[name])
     kw.update(over)
     return make_inputs(**kw)
+
+
+# ----------------------------------------------------------------------------------
+# FP8 (OCP E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, exponent
+# field 0 for subnormals m * 2^-9, codes 0x7f / 0xff NaN, no infinities, max 448)
+# ----------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def f64_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite values with |x| <= 448 to E4M3 (nearest, ties to even); uint8 codes.
+
+    Normal range: the spacing of representable values in [2^e, 2^(e+1)) is 2^(e-3);
+    below 2^-6 (subnormals) it is 2^-9. Rounding is np.rint on the value divided by
+    its spacing (exact power-of-two scaling), which rounds ties to even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)) or np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("E4M3 input must be finite with |x| <= 448")
+    sign = np.signbit(x)
+    a = np.abs(x)
+    _, e2 = np.frexp(a)                       # a = f * 2^e2, f in [0.5, 1)
+    e = np.maximum(e2 - 1, -6)                # exponent of the binade; subnormals use -6
+    spacing = np.ldexp(1.0, e - 3)
+    n = np.rint(a / spacing)                  # integer multiple of the spacing
+    # n in [8, 16] for normals (16 = carry into the next binade), [0, 8] below 2^-6
+    carry = n >= 16
+    e = np.where(carry, e + 1, e)
+    n = np.where(carry, n / 2, n)
+    normal = n >= 8
+    code = np.where(normal, ((e + 7) << 3) + (n - 8), n).astype(np.int64)
+    code = np.where(a == 0, 0, code)
+    if np.any(code > 0x7E):
+        raise ValueError("value rounds past 448")
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+@dataclass
+class Fp8Inputs:
+    """One seeded FP8 problem: q/k/v uint8 E4M3 codes and float32 descales; the true
+    tensors are descale * decoded codes."""
+
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    scale: float
+    seed: int
+    kind: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    descale_q: float
+    descale_k: float
+    descale_v: float
+
+
+def _quantize_per_tensor(x: np.ndarray):
+    amax = float(np.max(np.abs(x)))
+    s = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    y = np.clip(x.astype(np.float64) / float(s), -E4M3_MAX, E4M3_MAX)
+    return f64_to_e4m3_bits(y), float(s)
+
+
+def make_fp8_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, *,
+                    causal: bool, seed: int, kind: str = "gauss",
+                    scale: Optional[float] = None) -> Fp8Inputs:
+    """Draw an FP8 problem from ``default_rng(seed)`` (order Q, K, V).
+
+    kind "gauss": standard normal Q, K, V, each quantised with its own scale
+    amax / 448 (the float32 descale returned). ``scale`` defaults to 1/sqrt(d).
+
+    kind "signs": every Q row has exactly 4 entries of +-1 (random positions and
+    signs) and zeros elsewhere; K entries are -1, 0, +1 with probability 1/3 each; V is
+    quantised normal as above; descale_q = descale_k = 1 and scale = float32(ln 2).
+    Every score q.k is then an integer in [-4, 4] and scale * log2(e) is 1 up to
+    float32 rounding, so each softmax weight 2^(s - m), taken against any base m within
+    8 of the scores, is a power of two that E4M3 holds exactly.
+    """
+    rng = np.random.default_rng(seed)
+    shp_q, shp_kv = (B, Hq, Nq, d), (B, Hkv, Nk, d)
+    if kind == "gauss":
+        q, dq = _quantize_per_tensor(rng.standard_normal(shp_q, dtype=np.float32))
+        k, dk = _quantize_per_tensor(rng.standard_normal(shp_kv, dtype=np.float32))
+        v, dv = _quantize_per_tensor(rng.standard_normal(shp_kv, dtype=np.float32))
+        sc = float(1.0 / np.sqrt(d)) if scale is None else float(scale)
+    elif kind == "signs":
+        if d < 4:
+            raise ValueError("signs needs d >= 4")
+        qv = np.zeros(shp_q)
+        pos = np.argsort(rng.random(shp_q), axis=-1)[..., :4]
+        sgn = rng.choice([-1.0, 1.0], size=shp_q[:-1] + (4,))
+        np.put_along_axis(qv, pos, sgn, axis=-1)
+        kv = rng.integers(-1, 2, size=shp_kv).astype(np.float64)
+        q, dq = f64_to_e4m3_bits(qv), 1.0
+        k, dk = f64_to_e4m3_bits(kv), 1.0
+        v, dv = _quantize_per_tensor(rng.standard_normal(shp_kv, dtype=np.float32))
+        sc = float(np.float32(np.log(2.0)))
+    else:
+        raise ValueError(kind)
+    return Fp8Inputs(B, Hq, Hkv, Nq, Nk, d, bool(causal), sc, seed, kind, q, k, v,
+                     float(dq), float(dk), float(dv))

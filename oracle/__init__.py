@@ -11,5 +11,6 @@ Modules:
   attention  exact forward/backward from the definition (numpy float64)
   online     the pages' block recurrences (v1 normalised, v2 deferred, pg2 batched)
   scalar     brute force with Python floats, math.fsum and math.exp
+  fp8        E4M3 decoding, the FP8 forward's reference and its weight-rounding bound
 """
-from . import attention, online, scalar  # noqa: F401
+from . import attention, fp8, online, scalar  # noqa: F401
