@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd/bwd TFLOP/s at 1 GPU and % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 2.4 GHz x 8192 dense fp8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "c5_bf16_causal_gqa_B2Hq32Hkv8N8192d128"
 KERNEL_SOURCES = {
@@ -175,7 +176,45 @@ def extras(torch, fa, iters=20):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
     out["v1_vs_v2"] = version_ablation(torch, fa, g)
+    out["fp8_forward"] = fp8_forward(torch, fa, g, out)
     return out
+
+
+def fp8_forward(torch, fa, g, bf16_results, iters=20):
+    """fa_fwd_fp8 on the shapes of the d=128 causal bf16 forward workloads: E4M3 inputs
+    from seeded torch.randn scaled by 32 (per-tensor descale 1/32), FLOPs counted as for
+    bf16, against the dense FP8 MFMA peak, with the speedup over fa_fwd on the same
+    shape."""
+    res = {}
+    for name in ("c3a_bf16_causal_B4H32N4096d128", "c4a_bf16_causal_B1H8N32768d128"):
+        from exact_tiled_attention_36_amd import synth
+        w = synth.WORKLOADS[name]
+        B, Hq, Hkv, Nq, Nk, d, causal = (w[x] for x in ("B", "Hq", "Hkv", "Nq", "Nk", "d", "causal"))
+        mk = lambda *shape: (torch.randn(*shape, device="cuda", generator=g) * 32).to(torch.float8_e4m3fn)
+        q, k, v = mk(B, Hq, Nq, d), mk(B, Hkv, Nk, d), mk(B, Hkv, Nk, d)
+        o = torch.empty(B, Hq, Nq, d, device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty(B, Hq, Nq, device="cuda", dtype=torch.float32)
+        call = lambda: fa.fwd_fp8(q, k, v, 1 / 32, 1 / 32, 1 / 32, causal=causal, out=o, lse=lse)
+        for _ in range(5):
+            call()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(iters):
+            call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
+        rec = {"workload": name.replace("bf16", "fp8"), "ms": round(ms, 4),
+               "tflops": round(fl / ms / 1e9, 1),
+               "pct_fp8_peak": round(fl / ms / 1e9 / PEAK_FP8_TFLOPS * 100, 2)}
+        if name in bf16_results:
+            rec["speedup_over_bf16_fwd"] = round(bf16_results[name]["ms"] / ms, 3)
+        res[name.replace("bf16", "fp8")] = rec
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return res
 
 
 def version_ablation(torch, fa, g, iters=5, reps=5):

@@ -65,7 +65,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: problem exceeds the library's index range";
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";
-    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale (and every FP8 descale) must be finite and > 0";
     case FA_ERR_STAGE: return "FA_ERR_STAGE: backward stage must be 0, 1 or 2";
     case FA_ERR_VARIANT: return "FA_ERR_VARIANT: forward variant must be 0, 1, 2 or 3";
     default: return "unknown fa status code";
@@ -83,6 +83,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return launch_status(fa::launch_fwd_bf16(
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
       shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), (hipStream_t)stream));
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int Hq, int Hkv, int Nq, int Nk, int d, float scale, float descale_q,
+               float descale_k, float descale_v, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  for (float x : {descale_q, descale_k, descale_v})
+    if (!(x > 0.f) || !isfinite(x)) return FA_ERR_SCALE;
+  // the kernel folds scale * descale_q * descale_k into one float
+  const float c = scale * descale_q * descale_k;
+  if (!(c > 0.f) || !isfinite(c * 1.4426950408889634f)) return FA_ERR_SCALE;
+  if (!supported_bf16_dim(d)) return FA_ERR_HEAD_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  return launch_status(fa::launch_fwd_fp8(
+      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, descale_q,
+      descale_k, descale_v, shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), (hipStream_t)stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,

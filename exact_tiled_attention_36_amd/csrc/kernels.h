@@ -28,6 +28,12 @@ size_t fwd_v1_workspace_floats(const AttnShape& s);
 hipError_t launch_fwd_v1(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                          float* lse, float* ws, const AttnShape& s, hipStream_t st);
 
+// Forward, FP8 E4M3 (OCP) q/k/v bytes with per-tensor descales, bf16 o, fp32 lse
+// (d in {64,128,256}).
+hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o,
+                          float* lse, float descale_q, float descale_k, float descale_v,
+                          const AttnShape& s, hipStream_t st);
+
 // Forward, fp32 in/out (d % 4 == 0, d <= 256).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
                           float* lse, const AttnShape& s, hipStream_t st);

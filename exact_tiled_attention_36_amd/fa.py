@@ -28,6 +28,8 @@ _SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
     "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
     "fa_fwd_f32": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "fa_fwd_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float] * 4
+                   + [_c_int, _vp]),
     "fa_splitkv_default_splits": (_c_int, [_c_int] * 6),
     "fa_fwd_splitkv_workspace_bytes": (_c_size, [_c_int] * 7),
     "fa_fwd_splitkv": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6
@@ -104,6 +106,31 @@ def _dims(q, k, v):
     return B, Hq, Hkv, Nq, Nk, d
 
 
+def _buf(t, shape, dtype, device, name: str):
+    """Allocate an output buffer, or check that the caller's one fits exactly: the
+    library writes every element of it, so a smaller or strided buffer would be
+    overrun."""
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
+                         f"{tuple(shape)} on {device}")
+    return t
+
+
+def _workspace(t, nbytes: int, device):
+    """A byte workspace of at least nbytes (allocated if None)."""
+    import torch
+    if t is None:
+        return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.device != device
+            or not t.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    return t
+
+
 def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
         out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """O and LSE for bf16 (fa_fwd) or float32 (fa_fwd_f32) inputs."""
@@ -111,10 +138,8 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
     lib = load()
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buf(out, q.shape, q.dtype, q.device, "out")
+    lse = _buf(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     if q.dtype == torch.bfloat16:
         fn, name = lib.fa_fwd, "fa_fwd"
     elif q.dtype == torch.float32:
@@ -124,6 +149,29 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
     st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)), _stream(q.device))
     _check(name, st)
+    return out, lse
+
+
+def fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float,
+            causal: bool = False, scale: Optional[float] = None, out=None,
+            lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O (bf16) and LSE (float32) from FP8 E4M3 inputs with per-tensor descales
+    (fa_fwd_fp8): the attention of descale_q*q8, descale_k*k8, descale_v*v8.
+
+    q8/k8/v8 are uint8 tensors of E4M3 codes or torch.float8_e4m3fn tensors."""
+    import torch
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q8, k8, v8)
+    if q8.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError("fwd_fp8 takes uint8 E4M3 codes or float8_e4m3fn tensors")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = _buf(out, (B, Hq, Nq, d), torch.bfloat16, q8.device, "out")
+    lse = _buf(lse, (B, Hq, Nq), torch.float32, q8.device, "lse")
+    st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc, float(descale_q),
+                        float(descale_k), float(descale_v), int(bool(causal)),
+                        _stream(q8.device))
+    _check("fa_fwd_fp8", st)
     return out, lse
 
 
@@ -143,13 +191,11 @@ def fwd_variant(q, k, v, variant, causal: bool = False, scale: Optional[float] =
     if q.dtype != torch.bfloat16:
         raise ValueError("fwd_variant takes bfloat16 inputs")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buf(out, q.shape, q.dtype, q.device, "out")
+    lse = _buf(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     nbytes = lib.fa_fwd_variant_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, var)
-    if workspace is None and nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None or nbytes:
+        workspace = _workspace(workspace, nbytes, q.device)
     wptr = workspace.data_ptr() if workspace is not None else None
     wlen = workspace.numel() if workspace is not None else 0
     st = lib.fa_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -176,13 +222,10 @@ def fwd_splitkv(q, k, v, causal: bool = True, scale: Optional[float] = None,
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if q.dtype != torch.bfloat16:
         raise ValueError("fa_fwd_splitkv takes bfloat16")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buf(out, q.shape, q.dtype, q.device, "out")
+    lse = _buf(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     nbytes = lib.fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)),
                             int(num_splits), workspace.data_ptr(), workspace.numel(),
@@ -205,17 +248,14 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     lib = load()
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    for name, t in (("o", o), ("do", do)):
-        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must match q")
-    if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 [B, Hq, Nq]")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    o = _buf(o, q.shape, q.dtype, q.device, "o")
+    do = _buf(do, q.shape, q.dtype, q.device, "do")
+    lse = _buf(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
+    dq = _buf(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _buf(dk, k.shape, k.dtype, k.device, "dk")
+    dv = _buf(dv, v.shape, v.dtype, v.device, "dv")
     nbytes = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, Nq, Nk, d, sc,

@@ -58,7 +58,7 @@ enum {
   FA_ERR_LAUNCH = -7,     /* the HIP runtime rejected a kernel launch            */
   FA_ERR_TOO_LARGE = -8,  /* an index would overflow 32/64-bit addressing limits */
   FA_ERR_SPLITS = -9,     /* num_splits out of range                             */
-  FA_ERR_SCALE = -10,     /* scale is not a finite number > 0                    */
+  FA_ERR_SCALE = -10,     /* scale (or an FP8 descale) is not a finite number > 0 */
   FA_ERR_STAGE = -11,     /* fa_bwd_stage: stage not in {0, 1, 2}                */
   FA_ERR_VARIANT = -12    /* fa_fwd_variant: variant not in {0, 1, 2, 3}         */
 };
@@ -87,6 +87,30 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                void* stream);
+
+/*
+ * Forward pass with FP8 inputs: q, k, v hold OCP E4M3 bytes (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; no infinities; 0x7f and 0xff are NaN; largest finite
+ * value 448) with one scale per tensor, so the attention computed is that of
+ *     q = descale_q * Q8,  k = descale_k * K8,  v = descale_v * V8
+ * with the given `scale` on the scores, exactly as fa_fwd defines it. This is the
+ * low-precision forward the wiki lists for the third version ("FlashAttention"
+ * (newton.com.tw), 發展歷程); the pages do not give its scaling recipe, so the plain
+ * per-tensor form is used. Both products run on FP8 matrix instructions with fp32
+ * accumulation; the softmax weights are rounded to E4M3 (nearest even) before the
+ * product with V: for a row i and column c, |o_ic - exact| <= sum_j |P8_ij - P_ij| |v_jc|,
+ * where the weight's rounding error |P8 - P| is at most max(P / 16, 2^-10 P_max_i).
+ * The FP8 matrix instruction also sums its products with less than float32 accuracy
+ * (measured: up to about 2^-15 of sum_d |q_d k_d| per score), which moves scores, lse
+ * and weights slightly. lse is the float32 log-sum-exp of the unrounded weights, o is
+ * bf16. Output layouts, alignment, ownership and errors as
+ * fa_fwd (layouts count elements: q/k/v rows are d bytes); d must be 64, 128 or 256.
+ * FA_ERR_SCALE if a descale or scale * descale_q * descale_k * log2(e) is not a finite
+ * number > 0. NaN codes in the inputs propagate to the outputs of the rows they reach.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, float descale_q,
+               float descale_k, float descale_v, int causal, void* stream);
 
 /*
  * Split-KV forward for short query blocks (decode). Same result and layouts as

@@ -149,3 +149,36 @@ def test_fwd_variant_validation(lib):
     nows = [P, P, P, P, P, NULL, ws, 1, 2, 1, 8, 8, 128, 0.1, 1]
     assert lib.fa_fwd_variant(*nows, 2, None) == -6
     assert lib.fa_fwd_variant(NULL, *args[1:], 1, None) == -1
+
+
+def test_fwd_fp8_validation(lib):
+    def call(q=P, o=P, d=128, scale=0.1, dq=1.0, dk=1.0, dv=1.0, Hq=2, Hkv=1):
+        return lib.fa_fwd_fp8(q, P, P, o, P, 1, Hq, Hkv, 8, 8, d, scale, dq, dk, dv, 1, None)
+    assert call(q=NULL) == -1
+    assert call(Hq=3, Hkv=2) == -3
+    assert call(d=96) == -4
+    assert call(q=PU) == -5
+    assert call(o=PU) == -5
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(dq=bad) == -10
+        assert call(dk=bad) == -10
+        assert call(dv=bad) == -10
+        assert call(scale=bad) == -10
+    # the folded score scale must stay a finite positive float
+    assert call(scale=1e30, dq=1e30, dk=1e30) == -10
+    assert call(scale=1e-30, dq=1e-30, dk=1e-30) == -10
+
+
+def test_binding_rejects_wrong_output_buffers():
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cpu")
+    with pytest.raises(ValueError):
+        fa._buf(torch.empty(2, 3), (2, 4), torch.float32, dev, "out")
+    with pytest.raises(ValueError):
+        fa._buf(torch.empty(4, 2).t(), (2, 4), torch.float32, dev, "out")
+    with pytest.raises(ValueError):
+        fa._buf(torch.empty(2, 4, dtype=torch.float64), (2, 4), torch.float32, dev, "out")
+    t = torch.empty(2, 4)
+    assert fa._buf(t, (2, 4), torch.float32, dev, "out") is t
+    with pytest.raises(ValueError):
+        fa._workspace(torch.empty(16, dtype=torch.float32), 16, dev)
