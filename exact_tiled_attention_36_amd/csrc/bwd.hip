@@ -14,14 +14,17 @@
 //  1. bwd_pre:  D for every query row (HBM-bound row dot products).
 //  2. bwd_dkdv: one workgroup per (batch, kv-head, 128 keys); each wave keeps 32 keys
 //     of K and V in registers and loops over the group's query heads and the query
-//     blocks that can see its keys, with Q/dO/LSE/D tiles double buffered in LDS.
+//     blocks that can see its keys (diagonal blocks first, then the unmasked ones
+//     block by block from the last down, all heads of the group per block, so the
+//     group's waves share Q/dO tiles in L2), with Q/dO/LSE/D tiles triple buffered in
+//     LDS.
 //     S = Q K^T and dP = dO V^T come out with one key per lane, so P and dS (rounded
 //     to bf16) feed dV^T += dO^T P and dK^T += Q^T dS directly as B operands; dO^T
 //     and Q^T are read with LDS transpose loads.
-//  3. bwd_dq:   one workgroup per (batch, head, 128 queries); Q and dO stay in
-//     registers, K/V tiles are double buffered in LDS; S^T and dP^T put one query per
-//     lane, so LSE and D are per-lane scalars, and dQ^T += K^T dS^T reads K^T with
-//     LDS transpose loads.
+//  3. bwd_dq:   one workgroup per (batch, head, 32 queries per wave: 256 at d <= 128,
+//     128 at d = 256); Q and dO stay in registers, K/V tiles are triple buffered in
+//     LDS; S^T and dP^T put one query per lane, so LSE and D are per-lane scalars, and
+//     dQ^T += K^T dS^T reads K^T with LDS transpose loads.
 // No atomics: every output element is written by exactly one workgroup, so results
 // are bitwise reproducible.
 #include "common.h"
