@@ -540,7 +540,15 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   // buffer t%3 holds the K tile of key tile t, followed by its V tile
   auto Kb = [&](int t) FA_INLINE { return smem + (t % NB) * 2 * TILE; };
   // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
+  const uint32_t lane_off = 4u * lane;
   auto load_tile = [&](int t) FA_INLINE {
+    if constexpr (D <= 128) {
+      if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
+        FullTileLoad<D, BN, NW>::run(Kg, t * BN, Kb(t), wu, lane_off);
+        FullTileLoad<D, BN, NW>::run(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
+        return;
+      }
+    }
     tile_load_async<D, BN, NW>(Kg, t * BN, p.Nk, Kb(t), wu, lane);
     tile_load_async<D, BN, NW>(Vg, t * BN, p.Nk, Kb(t) + TILE, wu, lane);
   };

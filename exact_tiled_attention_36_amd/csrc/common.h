@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -261,6 +263,54 @@ __device__ __forceinline__ void tile_load_async(const uint16_t* G, int j0, int n
     lds_dma_dword(src, dst);
   }
 }
+
+// The same copy for a tile whose ROWS rows all exist (j0 + ROWS <= nrows), d = 64 or
+// 128, in fewer instructions: piece i of wave wu lies 256*(wu + NW*i) bytes past the
+// tile's first row in global memory, so one scalar base per 4 KiB serves every piece
+// and the rest goes into the instruction's immediate offset (which the hardware also
+// adds to the LDS address, so M0 is lowered by it); the LDS offset of piece i from the
+// wave's first piece is the same for every wave (checked at compile time), a
+// constant added to M0. About three scalar instructions per piece, no vector ones.
+template <int D, int ROWS, int NW>
+struct FullTileLoad {
+  static_assert(D == 64 || D == 128, "one piece per row or row pair");
+  using TL = TileLayout<D>;
+  static constexpr int RPP = D == 64 ? 2 : 1;   // rows per 256-byte piece
+  static constexpr int NSEG = ROWS / RPP;
+  static constexpr int NI = NSEG / NW;
+  static_assert(NSEG % NW == 0, "pieces must split evenly over the waves");
+  // byte offset in LDS of piece i of wave w, relative to the wave's first piece
+  static constexpr int lds_off(int w, int i) {
+    return 2 * (TL::row((w + NW * i) * RPP) - TL::row(w * RPP));
+  }
+  static constexpr bool wave_independent() {
+    for (int i = 0; i < NI; ++i)
+      for (int w = 1; w < NW; ++w)
+        if (lds_off(w, i) != lds_off(0, i)) return false;
+    return true;
+  }
+  static_assert(wave_independent(), "LDS offsets must not depend on the wave");
+
+  template <int I>
+  __device__ __forceinline__ static void piece(const char* g0, uint32_t lane_off, uint32_t m0) {
+    constexpr int GOFF = 256 * NW * I;
+    constexpr int IMM = GOFF % 4096;
+    static_assert(lds_off(0, I) >= IMM, "M0 stays at or above the tile's first piece");
+    lds_dma_row_imm<IMM>(g0 + (GOFF - IMM), lane_off, m0 + (uint32_t)(lds_off(0, I) - IMM));
+  }
+  template <int... I>
+  __device__ __forceinline__ static void all(const char* g0, uint32_t lane_off, uint32_t m0,
+                                             std::integer_sequence<int, I...>) {
+    (piece<I>(g0, lane_off, m0), ...);
+  }
+  // G: first row of the head; lds: the tile; wu: wave index (uniform); lane_off = 4*lane
+  __device__ __forceinline__ static void run(const uint16_t* G, int j0, uint16_t* lds, int wu,
+                                             uint32_t lane_off) {
+    const char* g0 = (const char*)(G + (size_t)j0 * D) + 256 * wu;
+    const uint32_t m0 = lds_addr(lds) + 2 * TL::row(wu * RPP);
+    all(g0, lane_off, m0, std::make_integer_sequence<int, NI>());
+  }
+};
 
 // Wait until this wave's vector memory operations (including direct LDS loads) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

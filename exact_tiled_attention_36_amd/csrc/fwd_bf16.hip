@@ -144,7 +144,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   auto Vb = [&](int i) FA_INLINE { return smem + (2 + (i & 1)) * TILE; };
   // Rows past the last key re-read the last key row: always finite, and masked to
   // zero weight before they can contribute (tiles past the end are never used).
+  const uint32_t lane_off = 4u * lane;
   auto load = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
+    if constexpr (D <= 128) {
+      if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
+        FullTileLoad<D, BN, NW>::run(G, t * BN, dst, wu, lane_off);
+        return;
+      }
+    }
     tile_load_async<D, BN, NW>(G, t * BN, p.Nk, dst, wu, lane);
   };
 
