@@ -544,8 +544,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   auto load_tile = [&](int t) FA_INLINE {
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
-        FullTileLoad<D, BN, NW>::run(Kg, t * BN, Kb(t), wu, lane_off);
-        FullTileLoad<D, BN, NW>::run(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
+        tile_load_full<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
+        tile_load_full<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
         return;
       }
     }

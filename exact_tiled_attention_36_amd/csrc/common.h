@@ -264,24 +264,23 @@ __device__ __forceinline__ void tile_load_async(const uint16_t* G, int j0, int n
   }
 }
 
-// The same copy for a tile whose ROWS rows all exist (j0 + ROWS <= nrows), d = 64 or
-// 128, in fewer instructions: piece i of wave wu lies 256*(wu + NW*i) bytes past the
-// tile's first row in global memory, so one scalar base per 4 KiB serves every piece
-// and the rest goes into the instruction's immediate offset (which the hardware also
-// adds to the LDS address, so M0 is lowered by it); the LDS offset of piece i from the
-// wave's first piece is the same for every wave (checked at compile time), a
-// constant added to M0. About three scalar instructions per piece, no vector ones.
-template <int D, int ROWS, int NW>
-struct FullTileLoad {
-  static_assert(D == 64 || D == 128, "one piece per row or row pair");
-  using TL = TileLayout<D>;
-  static constexpr int RPP = D == 64 ? 2 : 1;   // rows per 256-byte piece
-  static constexpr int NSEG = ROWS / RPP;
+// The same copy for a tile whose ROWS rows all exist (j0 + ROWS <= nrows), in fewer
+// instructions. L describes the LDS layout: L::RPP rows per 256-byte piece (contiguous
+// in global memory and in LDS) and L::row_bytes(r), the byte offset of row r. Piece i
+// of wave wu lies 256*(wu + NW*i) bytes past the tile's first row in global memory, so
+// one scalar base per 4 KiB serves every piece and the rest goes into the
+// instruction's immediate offset (which the hardware also adds to the LDS address, so
+// M0 is lowered by it); the LDS offset of piece i from the wave's first piece is the
+// same for every wave (checked at compile time), a constant added to M0. About three
+// scalar instructions per piece, no vector ones.
+template <class L, int ROWS, int NW>
+struct PieceCopy {
+  static constexpr int NSEG = ROWS / L::RPP;
   static constexpr int NI = NSEG / NW;
   static_assert(NSEG % NW == 0, "pieces must split evenly over the waves");
   // byte offset in LDS of piece i of wave w, relative to the wave's first piece
   static constexpr int lds_off(int w, int i) {
-    return 2 * (TL::row((w + NW * i) * RPP) - TL::row(w * RPP));
+    return L::row_bytes((w + NW * i) * L::RPP) - L::row_bytes(w * L::RPP);
   }
   static constexpr bool wave_independent() {
     for (int i = 0; i < NI; ++i)
@@ -303,14 +302,30 @@ struct FullTileLoad {
                                              std::integer_sequence<int, I...>) {
     (piece<I>(g0, lane_off, m0), ...);
   }
-  // G: first row of the head; lds: the tile; wu: wave index (uniform); lane_off = 4*lane
-  __device__ __forceinline__ static void run(const uint16_t* G, int j0, uint16_t* lds, int wu,
+  // row0: the tile's first row in global memory; lds: the tile; wu: wave index
+  // (uniform); lane_off = 4*lane
+  __device__ __forceinline__ static void run(const void* row0, void* lds, int wu,
                                              uint32_t lane_off) {
-    const char* g0 = (const char*)(G + (size_t)j0 * D) + 256 * wu;
-    const uint32_t m0 = lds_addr(lds) + 2 * TL::row(wu * RPP);
+    const char* g0 = (const char*)row0 + 256 * wu;
+    const uint32_t m0 = lds_addr(lds) + L::row_bytes(wu * L::RPP);
     all(g0, lane_off, m0, std::make_integer_sequence<int, NI>());
   }
 };
+
+// Rows of a bf16 TileLayout<D> as PieceCopy sees them (d = 64 or 128).
+template <int D>
+struct BfRows {
+  static_assert(D == 64 || D == 128, "one piece per row or row pair");
+  static constexpr int RPP = D == 64 ? 2 : 1;
+  static constexpr int row_bytes(int r) { return 2 * TileLayout<D>::row(r); }
+};
+
+// Whole bf16 tile: rows j0 .. j0+ROWS-1 of G, all present.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_load_full(const uint16_t* G, int j0, uint16_t* lds, int wu,
+                                               uint32_t lane_off) {
+  PieceCopy<BfRows<D>, ROWS, NW>::run(G + (size_t)j0 * D, lds, wu, lane_off);
+}
 
 // Wait until this wave's vector memory operations (including direct LDS loads) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

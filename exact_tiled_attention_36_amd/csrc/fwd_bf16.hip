@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   auto load = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
-        FullTileLoad<D, BN, NW>::run(G, t * BN, dst, wu, lane_off);
+        tile_load_full<D, BN, NW>(G, t * BN, dst, wu, lane_off);
         return;
       }
     }
