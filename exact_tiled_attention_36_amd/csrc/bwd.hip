@@ -160,20 +160,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   const int nu = qe > qd ? qe - qd : 0;        // unmasked tiles per head
   const int nm = (nqb - qb0) - nu;             // masked tiles per head
   const int total_m = nm * p.g, total = (nm + nu) * p.g;
-  // step -> (head in the group, first query row)
-  auto step_pos = [&](int s, int& hs, int& i0) FA_INLINE {
-    if (s < total_m) {
-      hs = s / nm;
-      const int j = s % nm;
-      i0 = (j < qd - qb0 ? qb0 + j : max(qd, qe) + (j - (qd - qb0))) * BMQ;
-    } else {
-      // unmasked tiles tile-major from the last one down, all heads of the group per
-      // tile: the workgroups of a (batch, kv-head) then read the same Q/dO tiles at
-      // about the same time, so most copies hit in L2
-      const int t = s - total_m;
-      hs = t % p.g;
-      i0 = (qe - 1 - t / p.g) * BMQ;
+  // Step cursor: step s, head hs in the group and tile counter j, advanced one step at
+  // a time without divisions. Masked steps run head by head over the nm masked tiles
+  // of each head (j = masked tile); unmasked steps run tile-major from the last tile
+  // down, all heads of the group per tile (j = tiles done): the workgroups of a
+  // (batch, kv-head) then read the same Q/dO tiles at about the same time, so most
+  // copies hit in L2.
+  struct Cur {
+    int s, hs, j;
+  };
+  auto cur_i0 = [&](const Cur& c) FA_INLINE {
+    if (c.s < total_m)
+      return (c.j < qd - qb0 ? qb0 + c.j : max(qd, qe) + (c.j - (qd - qb0))) * BMQ;
+    return (qe - 1 - c.j) * BMQ;
+  };
+  auto cur_next = [&](Cur& c) FA_INLINE {
+    if (c.s < total_m) {
+      if (++c.j == nm) {
+        c.j = 0;
+        ++c.hs;
+      }
+      if (c.s + 1 == total_m) c.hs = c.j = 0;
+    } else if (++c.hs == p.g) {
+      c.hs = 0;
+      ++c.j;
     }
+    ++c.s;
   };
 
   f32x16_t dkacc[NCB], dvacc[NCB];
@@ -200,16 +212,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     const float* dvec;
     int i0;
   };
-  auto pos_of = [&](int s) FA_INLINE {
-    int hs, i0;
-    step_pos(s, hs, i0);
-    const size_t hbase = (size_t)(b * p.Hq + kvh * p.g + hs) * p.Nq;
+  auto pos_of = [&](const Cur& c) FA_INLINE {
+    const size_t hbase = (size_t)(b * p.Hq + kvh * p.g + c.hs) * p.Nq;
     StepPos sp;
     sp.q = p.q + hbase * D;
     sp.dO = p.dO + hbase * D;
     sp.lse2 = p.lse2v + hbase;
     sp.dvec = p.dvec + hbase;
-    sp.i0 = i0;
+    sp.i0 = cur_i0(c);
     return sp;
   };
   auto dma_piece = [&](int s, const StepPos& ps, int j) FA_INLINE {
@@ -240,28 +250,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     for (int j = 0; j < 2 * PPW; ++j) dma_piece(s, ps, j);
     dma_stats(s, ps);
   };
-  auto issue = [&](int s) FA_INLINE { issue_at(s, pos_of(s)); };
   // Copies of a tile whose rows all lie below Nq, for D = 128: wave w copies rows
-  // w + 4i (i < 16) of Q and dO. Rows w+16a+4c share one scalar base, the immediate
-  // offset 1024c selects the row (it moves the LDS address by as much), and the LDS
-  // row offset is a per-wave base plus a constant, so a piece costs three scalar
-  // instructions.
+  // w + 16a + 4c (a, c < 4) of Q and dO. The four rows of one a share one M0 value (the
+  // LDS address of row w + 16a): row c sits 1296c bytes above it in LDS (4 rows of 256
+  // bytes plus 272 of padding, the same for every wave) and 1024c bytes above it in
+  // global memory, so the immediate offset is 1296c and the per-lane offset 272c
+  // smaller; the global base is lowered by 1024 to keep those offsets non-negative.
+  // Each group of four copies costs one M0 write and a few scalar adds.
+  static_assert(D != 128 || (TL::row(4) - TL::row(0) == 648 && TL::row(12) - TL::row(8) == 648 &&
+                             TL::row(19) - TL::row(3) == 2560),
+                "row offsets the grouped copies assume");
+  const uint32_t vo0 = lane_off + 1024u, vo1 = lane_off + 1024u - 272u,
+                 vo2 = lane_off + 1024u - 544u, vo3 = lane_off + 1024u - 816u;
   auto issue_full = [&](int s, const StepPos& ps) FA_INLINE {
     if constexpr (D == 128 && BMQ == 64) {
       const uint32_t qb = (uint32_t)(uintptr_t)(const FA_LDS void*)qtile(s) + 320u * wu;
-      const uint16_t* gq = ps.q + (size_t)(ps.i0 + wu) * D;
-      const uint16_t* go = ps.dO + (size_t)(ps.i0 + wu) * D;
+      const char* gq = (const char*)(ps.q + (size_t)(ps.i0 + wu) * D) - 1024;
+      const char* go = (const char*)(ps.dO + (size_t)(ps.i0 + wu) * D) - 1024;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const uint32_t m = qb + 5120u * a;
-        lds_dma_row_imm<0>(gq + 2048 * a, lane_off, m);
-        lds_dma_row_imm<0>(go + 2048 * a, lane_off, m + 2 * TILE);
-        lds_dma_row_imm<1024>(gq + 2048 * a, lane_off, m + 272);
-        lds_dma_row_imm<1024>(go + 2048 * a, lane_off, m + 272 + 2 * TILE);
-        lds_dma_row_imm<2048>(gq + 2048 * a, lane_off, m + 544);
-        lds_dma_row_imm<2048>(go + 2048 * a, lane_off, m + 544 + 2 * TILE);
-        lds_dma_row_imm<3072>(gq + 2048 * a, lane_off, m + 816);
-        lds_dma_row_imm<3072>(go + 2048 * a, lane_off, m + 816 + 2 * TILE);
+        lds_dma_row_x4<0, 1296, 2592, 3888>(gq + 4096 * a, vo0, vo1, vo2, vo3, m);
+        lds_dma_row_x4<0, 1296, 2592, 3888>(go + 4096 * a, vo0, vo1, vo2, vo3, m + 2 * TILE);
       }
       dma_stats(s, ps);
     } else {
@@ -414,26 +424,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     }
   };
 
+  Cur cur = {0, 0, 0};
   if (total > 0) {
-    issue(0);
+    issue_at(0, pos_of(cur));
     wait_vmem();
   }
   __syncthreads();
 
   // Step s copies the tiles of step s+1 into buffer (s+1)%3 first (tiles of the
-  // unmasked loop lie wholly below Nq).
+  // unmasked loop lie wholly below Nq). cur positions step s, nxt step s+1.
+  Cur nxt = cur;
+  cur_next(nxt);
   int s = 0;
   for (; s < total_m; ++s) {
-    if (s + 1 < total) issue(s + 1);
-    int hs, i0;
-    step_pos(s, hs, i0);
-    step(BoolC<true>(), s, i0);
+    if (s + 1 < total) issue_at(s + 1, pos_of(nxt));
+    step(BoolC<true>(), s, cur_i0(cur));
+    cur = nxt;
+    cur_next(nxt);
     wait_vmem();
     __syncthreads();
   }
   for (; s < total; ++s) {
-    if (s + 1 < total) issue_full(s + 1, pos_of(s + 1));
-    step(BoolC<false>(), s, (qe - 1 - (s - total_m) / p.g) * BMQ);
+    if (s + 1 < total) issue_full(s + 1, pos_of(nxt));
+    step(BoolC<false>(), s, cur_i0(cur));
+    cur = nxt;
+    cur_next(nxt);
     wait_vmem();
     __syncthreads();
   }

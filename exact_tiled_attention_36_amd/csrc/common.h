@@ -232,6 +232,26 @@ __device__ __forceinline__ void lds_dma_row_imm(const void* gbase, uint32_t lane
       : "m0");
 }
 
+// Four copies of the saddr form that share one M0 write: copy c reads
+// gbase + voff_c + IMM_c and writes LDS lds_m0 + IMM_c + 4*lane. With row strides that
+// differ between global memory and LDS, voff_c absorbs the difference.
+template <int I0, int I1, int I2, int I3>
+__device__ __forceinline__ void lds_dma_row_x4(const void* gbase, uint32_t v0, uint32_t v1,
+                                               uint32_t v2, uint32_t v3, uint32_t lds_m0) {
+  static_assert(I0 >= 0 && I3 < 4096 && I0 <= I1 && I1 <= I2 && I2 <= I3, "offset range");
+  asm volatile(
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %4 offset:%6\n\t"
+      "global_load_lds_dword %1, %4 offset:%7\n\t"
+      "global_load_lds_dword %2, %4 offset:%8\n\t"
+      "global_load_lds_dword %3, %4 offset:%9"
+      :
+      : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(gbase), "s"(lds_m0), "i"(I0), "i"(I1), "i"(I2),
+        "i"(I3)
+      : "m0");
+}
+
 // Asynchronous copy of a [ROWS][D] bf16 tile (global rows j0.. of G, clamped to
 // nrows-1) into an LDS tile, by direct global->LDS loads of 4 bytes per lane: each
 // wave instruction fills one contiguous 256-byte piece (128 elements). The NW waves of
