@@ -175,6 +175,7 @@ def extras(torch, fa, iters=20):
         out[name] = rec
         del q, k, v, o, lse
         torch.cuda.empty_cache()
+    out["decode_gqa_B16Hq32Hkv4Nq1Nk8192d128"] = gqa_decode(torch, fa, g, iters)
     out["v1_vs_v2"] = version_ablation(torch, fa, g)
     out["fp8_forward"] = fp8_forward(torch, fa, g, out)
     return out
@@ -215,6 +216,36 @@ def fp8_forward(torch, fa, g, bf16_results, iters=20):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
     return res
+
+
+def gqa_decode(torch, fa, g, iters):
+    """Split-KV decode with eight query heads per kv-head (the chunks run on the matrix
+    cores), in GB/s of Q, K, V, O and LSE moved once."""
+    B, Hq, Hkv, Nk, d = 16, 32, 4, 8192, 128
+    q = torch.randn(B, Hq, 1, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    k = torch.randn(B, Hkv, Nk, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    v = torch.randn(B, Hkv, Nk, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, 1, device="cuda", dtype=torch.float32)
+    ws = torch.empty(fa.splitkv_workspace_bytes(B, Hq, Hkv, 1, Nk, d), device="cuda",
+                     dtype=torch.uint8)
+    call = lambda: fa.fwd_splitkv(q, k, v, causal=True, out=o, lse=lse, workspace=ws)
+    for _ in range(5):
+        call()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(iters):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+            "pct_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS * 100, 2),
+            "kernel": "fa_fwd_splitkv (matrix-core chunks + merge)"}
 
 
 def version_ablation(torch, fa, g, iters=5, reps=5):

@@ -9,12 +9,14 @@
 // normalised output O_c and its log-sum-exp L_c; the merged result is
 // O = sum_c exp(L_c - L) O_c with L = log sum_c exp(L_c).
 //
-// Work is HBM-bound (about one flop per byte), so it stays on the vector ALUs: in a
-// chunk workgroup every key row is read by d/8 lanes (16 bytes each, coalesced),
-// scores are lane-group dot products finished with xor-shuffles, and each lane group
-// runs its own online softmax over its share of the keys. The group states are
-// merged through LDS at the end. All query rows of the kv-head (the GQA group times
-// Nq, at most 16) are handled by the same workgroup, so K and V are read once.
+// Work is HBM-bound (about one flop per byte per query row). All query rows of the
+// kv-head (the GQA group times Nq, at most 16) are handled by the same chunk, so K and
+// V are read once. With one row the chunk stays on the vector ALUs
+// (splitkv_chunk_kernel): every key row is read by d/8 lanes (16 bytes each,
+// coalesced), scores are lane-group dot products finished with xor-shuffles, each lane
+// group runs its own online softmax over its share of the keys, and the group states
+// are merged through LDS at the end. With several rows that vector work grows with the
+// row count and the chunk runs on the matrix cores instead (splitkv_mfma_kernel).
 #include "common.h"
 #include "kernels.h"
 
@@ -159,6 +161,149 @@ __global__ __launch_bounds__(256) void splitkv_chunk_kernel(SplitParams p) {
   }
 }
 
+// The same chunk results on the matrix cores, for several query rows per kv-head (GQA
+// groups, small query blocks): one wave per chunk holds the group's rows as the 32
+// columns of Sᵀ = K Qᵀ (rows past the group's are zeros and never stored), streams the
+// chunk's keys in tiles of 32 through its own double-buffered LDS tiles (direct copies,
+// no barriers: a wave waits only for its own copies), and runs the forward kernel's
+// per-tile steps: scores on v_mfma_f32_32x32x16_bf16, masking at the chunk end and the
+// causal limit of each row, the online softmax with the lazy rescale, and Oᵀ += Vᵀ Pᵀ
+// with Vᵀ read by LDS transpose loads. Row r of a kv-head is query head kvh*g + r/Nq,
+// query r % Nq.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void splitkv_mfma_kernel(SplitParams p) {
+  using TL = TileLayout<D>;
+  constexpr int BN = 32;
+  constexpr int TILE = TL::elems(BN);
+  constexpr int NDC = D / 16, NCB = D / 32;
+  static_assert(TL::shifts_ok(BN), "LDS reads add row offsets as constants");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // K0 V0 K1 V1
+
+  const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
+  const int split = blockIdx.x % p.splits;
+  const int bkv = blockIdx.x / p.splits;
+  const int kvh = bkv % p.Hkv, b = bkv / p.Hkv;
+  const int j_begin = split * p.chunk;
+  const int j_end = min(p.Nk, j_begin + p.chunk);
+
+  const bool rvalid = l32 < p.rows;
+  const int rr = rvalid ? l32 : 0;
+  const int h = kvh * p.g + rr / p.Nq, qi = rr % p.Nq;
+  const int lim = qi + p.causal_off;  // keys j <= lim are visible to this row
+  bf16x8_t qreg[NDC];
+  {
+    const u32x4_t* src = (const u32x4_t*)(p.q + ((size_t)(b * p.Hq + h) * p.Nq + qi) * D + 8 * hi);
+    const u32x4_t z = {0, 0, 0, 0};
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8_t, rvalid ? src[2 * dc] : z);
+  }
+
+  const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+  const uint16_t* Vg = p.v + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+  const int ntiles = j_end > j_begin ? (j_end - j_begin + BN - 1) / BN : 0;
+  auto Kb = [&](int t) FA_INLINE { return smem + (t & 1) * 2 * TILE; };
+  const uint32_t lane_off = 4u * lane;
+  // rows past Nk re-read the last key row; keys at or past the chunk end are masked
+  auto load = [&](int t) FA_INLINE {
+    const int j0 = j_begin + t * BN;
+    if constexpr (D <= 128) {
+      if (j0 + BN <= p.Nk) {
+        tile_load_full<D, BN, 1>(Kg, j0, Kb(t), 0, lane_off);
+        tile_load_full<D, BN, 1>(Vg, j0, Kb(t) + TILE, 0, lane_off);
+        return;
+      }
+    }
+    tile_load_async<D, BN, 1>(Kg, j0, p.Nk, Kb(t), 0, lane);
+    tile_load_async<D, BN, 1>(Vg, j0, p.Nk, Kb(t) + TILE, 0, lane);
+  };
+
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint32_t srow = 2 * (TL::row(l32) + 8 * hi);
+  const uint32_t trow = 2 * (TL::row(tr_row) + tr_col);
+
+  f32x16_t oacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+  const float c2 = p.scale_log2;
+
+  if (ntiles > 0) load(0);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmem();  // tile t is in LDS; the buffer of t+1 was last read in step t-1
+    if (t + 1 < ntiles) load(t + 1);
+    const uint16_t* Ks = Kb(t);
+    // Sᵀ = K Qᵀ: one row per lane, keys 8(r/4) + 4*hi + r%4 of the tile
+    f32x16_t sc = zero16();
+    {
+      const uint32_t base = opaque(lds_addr(Ks) + srow);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) sc = mfma32x32x16(lds_read8_at(base + 32 * dc), qreg[dc], sc);
+    }
+    const int j0 = j_begin + t * BN;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (j >= j_end || (CAUSAL && j > lim)) sc[r] = -INFINITY;
+      mx = fmaxf(mx, sc[r]);
+    }
+    mx = xhalf_max(mx) * c2;
+    // lazy rescale: the base moves only when some row's max passes it by more than 8
+    const bool move = __any(mx > m + 8.f);
+    const float m_next = move ? fmaxf(m, mx) : m;
+    const float m_use = m_next == -INFINITY ? 0.f : m_next;
+    if (move) {
+      const float alpha = fast_exp2(m - m_use);
+      lsum *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+    }
+    m = m_next;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(fmaf(sc[r], c2, -m_use));
+      const float p1 = fast_exp2(fmaf(sc[r + 1], c2, -m_use));
+      lsum += p0 + p1;
+      pk[r >> 1] = pack_bf16x2(p0, p1);
+    }
+    // Oᵀ += Vᵀ Pᵀ
+    const uint32_t vbase = opaque(lds_addr(Ks + TILE) + trow);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4_t bu = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
+      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bu);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const bf16x8_t a = join8(lds_read_tr4_at(vbase + 2 * (TL::row(16 * kk) + 32 * cb)),
+                                 lds_read_tr4_at(vbase + 2 * (TL::row(16 * kk + 8) + 32 * cb)));
+        oacc[cb] = mfma32x32x16(a, bop, oacc[cb]);
+      }
+    }
+  }
+
+  // normalised chunk output and its log-sum-exp
+  const float ltot = xhalf_sum(lsum);
+  if (rvalid) {
+    const size_t row = (size_t)(b * p.Hq + h) * p.Nq + qi;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float* po = p.part_o + (row * p.splits + split) * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4_t v4 = {oacc[cb][4 * rg] * inv, oacc[cb][4 * rg + 1] * inv,
+                            oacc[cb][4 * rg + 2] * inv, oacc[cb][4 * rg + 3] * inv};
+        *(f32x4_t*)(po + 32 * cb + 8 * rg + 4 * hi) = v4;
+      }
+    if (hi == 0)
+      p.part_lse[row * p.splits + split] = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
 // One wave per output row: merge the chunk results with weights exp(L_c - L).
 template <int D>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitParams p, int nrows) {
@@ -207,10 +352,27 @@ hipError_t run(const SplitParams& p, int B, hipStream_t st) {
 }
 
 template <int D>
+hipError_t run_mfma(const SplitParams& p, int B, hipStream_t st) {
+  const long long n = (long long)B * p.Hkv * p.splits;
+  if (n > 0x7fffffffLL || p.rows > 32) return hipErrorInvalidValue;
+  if (p.causal_off < 0x3fffffff)
+    hipLaunchKernelGGL((splitkv_mfma_kernel<D, true>), dim3((int)n), dim3(64), 0, st, p);
+  else
+    hipLaunchKernelGGL((splitkv_mfma_kernel<D, false>), dim3((int)n), dim3(64), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrows = B * p.Hq * p.Nq;
+  hipLaunchKernelGGL((splitkv_merge_kernel<D>), dim3((nrows + 3) / 4), dim3(256), 0, st, p, nrows);
+  return hipGetLastError();
+}
+
+// Measured on MI355X (d = 128): one row per kv-head, B8 H8 Nk32768: vector 5.7 TB/s,
+// matrix 5.4; four rows (Hq32 Hkv8, Nk65536): 4.5 vs 5.4; eight rows (Hq32 Hkv4,
+// Nk8192): 0.72 vs 5.2.
+template <int D>
 hipError_t run_rows(const SplitParams& p, int B, hipStream_t st) {
   if (p.rows <= 1) return run<D, 1>(p, B, st);
-  if (p.rows <= 4) return run<D, 4>(p, B, st);
-  return run<D, 16>(p, B, st);
+  return run_mfma<D>(p, B, st);
 }
 
 }  // namespace

@@ -32,6 +32,13 @@ def test_c4b_decode_full_size(gpu_lib):
     check(gpu_lib, inp, 0, "c4b")
 
 
+def test_gqa_decode_full_size(gpu_lib):
+    """Eight query heads per kv-head at one query each: the chunks run on the matrix
+    cores (rows of a kv-head = the GQA group)."""
+    inp = synth.make_inputs(16, 32, 4, 1, 8192, 128, causal=True, seed=4200)
+    check(gpu_lib, inp, 0, "gqa-decode")
+
+
 @pytest.mark.parametrize("case", [
     # B, Hq, Hkv, Nq, Nk, d, causal, splits
     (1, 32, 8, 1, 5000, 128, True, 0),      # GQA decode, 4 rows per kv head
@@ -41,6 +48,8 @@ def test_c4b_decode_full_size(gpu_lib):
     (1, 2, 2, 1, 10, 128, True, 6),         # a chunk past the last key stays empty
     (1, 2, 2, 1, 77, 64, True, 77),         # one key per chunk
     (1, 4, 1, 4, 2, 128, True, 2),          # Nq > Nk: rows that see no key
+    (2, 16, 1, 1, 1000, 64, False, 5),      # MQA, 16 rows per kv head
+    (1, 6, 3, 5, 333, 128, True, 3),        # 10 rows, ragged chunks and tiles
 ])
 def test_splitkv_shapes(gpu_lib, case):
     B, Hq, Hkv, Nq, Nk, d, causal, splits = case
