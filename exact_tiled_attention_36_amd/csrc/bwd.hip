@@ -412,10 +412,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       rd_ld(qs, 1);
       soft(qs, 0);
       interleave();
+      // keep the softmax in this region: its results are used only in the next
+      // step, and the compiler would otherwise sink it past the loop's branches
+      pin(pc[qs][0]);
+      pin(dsc[qs][0]);
       mm_g(ga[1], gb[1], qs == 0 ? pprev[1] : pc[qs - 1][1], qs == 0 ? dprev[1] : dsc[qs - 1][1]);
       if (qs + 1 < NQS) rd_s(qs + 1, 0);
       soft(qs, 1);
       interleave();
+      pin(pc[qs][1]);
+      pin(dsc[qs][1]);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {

@@ -85,6 +85,7 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 // be sunk past this point (e.g. across a barrier into the next loop iteration).
 __device__ __forceinline__ void pin(uint32_t x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(bf16x8_t x) { asm volatile("" ::"v"(x)); }
 
 __device__ __forceinline__ bf16x8_t lds_read8_at(uint32_t a) {
   return __builtin_bit_cast(bf16x8_t, *(const FA_LDS u32x4_t*)(uintptr_t)a);
