@@ -40,6 +40,11 @@
 namespace fa {
 namespace {
 
+#ifndef FWD_SMALL_GRID
+#define FWD_SMALL_GRID 256
+#endif
+constexpr long long kSmallGrid = FWD_SMALL_GRID;
+
 // Headroom (in log2 units) the running max may lag behind the true row max before
 // the accumulators are rescaled: weights stay below 2^8, far inside fp32/bf16 range.
 constexpr float kRescaleSlack = 8.f;
@@ -404,6 +409,14 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   p.causal_off = s.Nk - s.Nq;
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
+  // Grids too small to give every compute unit a 256-row workgroup (short sequences,
+  // few heads) use 128-row workgroups of 4 waves instead: twice the workgroups, each
+  // less efficient per unit of work, but no compute unit left idle.
+  const long long wg256 = (long long)((s.Nq + 255) / 256) * s.Hq * s.B;
+  if (wg256 < kSmallGrid && (s.d == 64 || s.d == 128)) {
+    if (s.d == 64) return c ? run<64, 64, 4, 1, true>(p, s.B, st) : run<64, 64, 4, 1, false>(p, s.B, st);
+    return c ? run<128, 64, 4, 1, true>(p, s.B, st) : run<128, 64, 4, 1, false>(p, s.B, st);
+  }
   switch (s.d) {
 #ifndef FWD_CFG128
 #define FWD_CFG128 64, 8, 1
