@@ -746,6 +746,13 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.scale = s.scale;
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
+  // dQ grids too small for one 256-row workgroup per compute unit use 128-row ones (4
+  // waves): twice the workgroups, no compute unit left idle (dK/dV is unchanged)
+  const long long dq256 = (long long)((s.Nq + 255) / 256) * s.Hq * s.B;
+  if (dq256 < 256 && (s.d == 64 || s.d == 128)) {
+    if (s.d == 64) return c ? run<64, 64, 32, 4, true>(p, s.B, stage, st) : run<64, 64, 32, 4, false>(p, s.B, stage, st);
+    return c ? run<128, 64, 32, 4, true>(p, s.B, stage, st) : run<128, 64, 32, 4, false>(p, s.B, stage, st);
+  }
   switch (s.d) {
     case 64: return c ? run<64, 64, 32, 8, true>(p, s.B, stage, st) : run<64, 64, 32, 8, false>(p, s.B, stage, st);
     case 128: return c ? run<128, 64, 32, 8, true>(p, s.B, stage, st) : run<128, 64, 32, 8, false>(p, s.B, stage, st);
