@@ -10,6 +10,11 @@
   the largest errors of round-to-nearest E4M3 as torch's cast rounds; it covers a
   simulated FP8 forward (weights against any base up to 8 below the row max, rounded
   by torch's cast); and a two-key case reaches 93% of it, so it is not slack.
+* The score-error bound: raising every score by its largest accumulation error moves
+  lse by between half of E and E.
+* Planted mistakes in copies of the decoder (exponent bias, mantissa scale, subnormal
+  scale), the bound (relative constant, absolute floor, signed V) and the score error
+  (4x too small or too large) each fail one of these pins.
 """
 import math
 
@@ -218,3 +223,145 @@ def test_bound_covers_score_errors_and_rounding(causal):
     np.testing.assert_allclose(
         F.score_error_rows(a.q, a.k, a.descale_q, a.descale_k, a.scale, causal, 0, 1, rows,
                            eps), E[0, 1, rows], rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------------
+# planted mistakes in copies of the FP8 oracle: each must fail one of the pins above
+# (restated here as functions of the code under test)
+# ----------------------------------------------------------------------------------
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _mut_decode(kind):
+    def dec(codes):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        bias = 8 if kind == "bias8" else 7
+        mden = 16.0 if kind == "mant16" else 8.0
+        sub_exp = -10 if kind == "sub_scale" else -9
+        normal = sign * np.ldexp(1.0 + m / mden, e - bias)
+        sub = sign * np.ldexp(m.astype(np.float64), sub_exp)
+        val = np.where(e == 0, sub, normal)
+        return np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return dec
+
+
+def pin_decoder(dec):
+    codes = np.arange(256, dtype=np.uint8)
+    mine = dec(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    ok = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+def _mut_bound(kind):
+    """p_rounding_bound with one planted mistake (float64, whole tensors)."""
+    def bound(q8, k8, v8, dq, dk, dv, scale, causal, acc_eps=0.0):
+        from oracle import attention as A
+        q, k, v = F.dequantize(q8, dq), F.dequantize(k8, dk), F.dequantize(v8, dv)
+        B, Hq, Nq, _ = q.shape
+        g = Hq // k.shape[1]
+        out = np.zeros(q.shape[:3] + (v.shape[3],))
+        u = 1 / 32 if kind == "u32" else 1 / 16
+        floor = 2.0 ** -14 if kind == "floor_small" else 2.0 ** -10
+        for b in range(B):
+            for h in range(Hq):
+                rows = np.arange(Nq)
+                s = A.scores(q[b, h], k[b, h // g], scale, rows, Nq, causal)
+                p = A.softmax_rows(s)[0]
+                pmax = p.max(axis=1, keepdims=True)
+                err = np.where(p > 0, np.maximum(p * u, floor * pmax), 0.0)
+                vv = v[b, h // g] if kind == "signed_v" else np.abs(v[b, h // g])
+                mag = np.abs(q[b, h]) @ np.abs(k[b, h // g]).T
+                mag = np.where(A.visible(rows, Nq, k.shape[2], causal), mag, 0.0)
+                E = acc_eps * scale * mag.max(axis=1)
+                grow = np.exp(2 * E)[:, None]
+                out[b, h] = grow * (err @ vv) + (grow - 1) * (p @ np.abs(v[b, h // g]))
+        return out
+    return bound
+
+
+def pin_bound_covers(bound):
+    """Simulated FP8 forwards (bases 0 and 8 below the row max, E4M3 rounding by
+    torch's cast; sharp scores where most weights are subnormal; perturbed scores)
+    stay within the bound."""
+    for seed, causal, mult in ((21, False, 1.0), (22, True, 1.0), (24, False, 6.0)):
+        a = synth.make_fp8_inputs(1, 2, 1, 70, 70, 64, causal=causal, seed=seed)
+        sc = a.scale * mult
+        o, _ = F.forward_fp8(a.q, a.k, a.v, a.descale_q, a.descale_k, a.descale_v, sc, causal)
+        bd = bound(a.q, a.k, a.v, a.descale_q, a.descale_k, a.descale_v, sc, causal)
+        aa = synth.Fp8Inputs(a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d, causal, sc, a.seed, a.kind,
+                             a.q, a.k, a.v, a.descale_q, a.descale_k, a.descale_v)
+        for drop in (np.zeros((1, 2, 70)), np.full((1, 2, 70), 8.0)):
+            sim = simulate_fp8_forward(aa, drop)
+            assert np.all(np.abs(sim - o) <= bd * (1 + 1e-9) + 1e-15)
+    eps = 2.0 ** -8
+    a = synth.make_fp8_inputs(1, 1, 1, 60, 60, 64, causal=False, seed=23)
+    q, k, v = (F.dequantize(x, s) for x, s in ((a.q, a.descale_q), (a.k, a.descale_k),
+                                               (a.v, a.descale_v)))
+    o, _ = F.forward_fp8(a.q, a.k, a.v, a.descale_q, a.descale_k, a.descale_v, a.scale, False)
+    bd = bound(a.q, a.k, a.v, a.descale_q, a.descale_k, a.descale_v, a.scale, False, eps)
+    s = a.scale * (q[0, 0] @ k[0, 0].T)
+    emax = eps * a.scale * (np.abs(q[0, 0]) @ np.abs(k[0, 0]).T)
+    sign = np.where(s >= np.median(s, axis=1, keepdims=True), 1.0, -1.0)
+    for sg in (sign, -sign):
+        sp = s + sg * emax
+        w = np.exp(sp - sp.max(axis=1, keepdims=True))
+        sim = (torch_round_e4m3(w) @ v[0, 0]) / w.sum(axis=1, keepdims=True)
+        assert np.all(np.abs(sim - o[0, 0]) <= bd[0, 0] * (1 + 1e-9) + 1e-12)
+
+
+def pin_score_error(score_error):
+    """All scores raised by their largest accumulation error move lse by a weighted mean
+    of those errors: at most E_i, and (the errors of one row's keys differ little) at
+    least half of it."""
+    eps = 2.0 ** -8
+    for causal in (False, True):
+        a = synth.make_fp8_inputs(1, 2, 1, 50, 50, 64, causal=causal, seed=25)
+        q, k = F.dequantize(a.q, a.descale_q), F.dequantize(a.k, a.descale_k)
+        _, lse = F.forward_fp8(a.q, a.k, a.v, a.descale_q, a.descale_k, a.descale_v,
+                               a.scale, causal)
+        E = score_error(a.q, a.k, a.descale_q, a.descale_k, a.scale, causal, eps)
+        for h in range(2):
+            s = a.scale * (q[0, h] @ k[0, 0].T)
+            emax = eps * a.scale * (np.abs(q[0, h]) @ np.abs(k[0, 0]).T)
+            if causal:
+                s = np.where(np.tri(50, dtype=bool), s, -np.inf)
+            sp = s + emax
+            m = sp.max(axis=1, keepdims=True)
+            lse_up = m[:, 0] + np.log(np.exp(sp - m).sum(axis=1))
+            shift = lse_up - lse[0, h]
+            assert np.all(shift <= E[0, h] * (1 + 1e-9) + 1e-15)
+            assert np.all(shift >= 0.5 * E[0, h])
+
+
+def test_pins_accept_the_oracle():
+    pin_decoder(F.e4m3_to_f64)
+    pin_bound_covers(F.p_rounding_bound)
+    pin_score_error(F.score_error)
+
+
+@pytest.mark.parametrize("kind", ["bias8", "mant16", "sub_scale"])
+def test_planted_decoder_mistakes_are_caught(kind):
+    assert _fails(pin_decoder, _mut_decode(kind))
+
+
+@pytest.mark.parametrize("kind", ["u32", "floor_small", "signed_v"])
+def test_planted_bound_mistakes_are_caught(kind):
+    assert _fails(pin_bound_covers, _mut_bound(kind))
+
+
+@pytest.mark.parametrize("factor", [0.25, 4.0])
+def test_planted_score_error_mistakes_are_caught(factor):
+    def wrong(*args):
+        return factor * F.score_error(*args)
+    assert _fails(pin_score_error, wrong)
