@@ -131,6 +131,28 @@ def cpu_baseline(inp, min_seconds=10.0):
                       "S and P materialised"}
 
 
+def timed_ms(torch, call, iters, warm_ms=50.0):
+    """Average milliseconds per call over iters calls on the current stream, after
+    warm-up calls until at least warm_ms of GPU time has passed (at least three), so
+    that short kernels are timed at the clock a sustained run reaches."""
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spent, n = 0.0, 0
+    while n < 3 or spent < warm_ms:
+        e0.record(st)
+        call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
+        n += 1
+    e0.record(st)
+    for _ in range(iters):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
 def extras(torch, fa, iters=20):
     """Forward throughput on the other workloads, decode in GB/s (seeded torch.randn)."""
     from exact_tiled_attention_36_amd import synth
@@ -154,16 +176,7 @@ def extras(torch, fa, iters=20):
             call = lambda: fa.fwd_splitkv(q, k, v, causal=causal, out=o, lse=lse, workspace=ws)
         else:
             call = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-        for _ in range(5):
-            call()
-        st = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(iters):
-            call()
-        e1.record(st)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
+        ms = timed_ms(torch, call, iters)
         fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
         rec = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
                "pct_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2)}
@@ -196,16 +209,7 @@ def fp8_forward(torch, fa, g, bf16_results, iters=20):
         o = torch.empty(B, Hq, Nq, d, device="cuda", dtype=torch.bfloat16)
         lse = torch.empty(B, Hq, Nq, device="cuda", dtype=torch.float32)
         call = lambda: fa.fwd_fp8(q, k, v, 1 / 32, 1 / 32, 1 / 32, causal=causal, out=o, lse=lse)
-        for _ in range(5):
-            call()
-        st = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(iters):
-            call()
-        e1.record(st)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
+        ms = timed_ms(torch, call, iters)
         fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
         rec = {"workload": name.replace("bf16", "fp8"), "ms": round(ms, 4),
                "tflops": round(fl / ms / 1e9, 1),
@@ -230,16 +234,7 @@ def gqa_decode(torch, fa, g, iters):
     ws = torch.empty(fa.splitkv_workspace_bytes(B, Hq, Hkv, 1, Nk, d), device="cuda",
                      dtype=torch.uint8)
     call = lambda: fa.fwd_splitkv(q, k, v, causal=True, out=o, lse=lse, workspace=ws)
-    for _ in range(5):
-        call()
-    st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(iters):
-        call()
-    e1.record(st)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    ms = timed_ms(torch, call, iters)
     nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
@@ -271,19 +266,10 @@ def version_ablation(torch, fa, g, iters=5, reps=5):
                          device="cuda", dtype=torch.uint8)
         fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
         times = {var: [] for var in range(4)}
-        st = torch.cuda.current_stream()
         for _ in range(reps):
             for var in range(4):
                 call = lambda: fa.fwd_variant(q, k, v, var, causal=causal, out=o, lse=lse, workspace=ws)
-                for _ in range(2):
-                    call()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(st)
-                for _ in range(iters):
-                    call()
-                e1.record(st)
-                torch.cuda.synchronize()
-                times[var].append(e0.elapsed_time(e1) / iters)
+                times[var].append(timed_ms(torch, call, iters, warm_ms=20.0))
         rec = {}
         for var in range(4):
             ms = statistics.median(times[var])
