@@ -99,6 +99,8 @@ def _dims(q, k, v):
             raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share a dtype")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     B, Hq, Nq, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
@@ -118,6 +120,24 @@ def _buf(t, shape, dtype, device, name: str):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
                          f"{tuple(shape)} on {device}")
     return t
+
+
+def _inp(t, shape, dtype, device, name: str):
+    """Check a required input tensor (never allocated: the library reads it)."""
+    import torch
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
+                         f"{tuple(shape)} on {device}")
+    return t
+
+
+def _launch(name: str, fn, device, *args):
+    """Call a library entry point with the tensors' device current (the library
+    launches on the current HIP device and the stream passed in) and raise on error."""
+    import torch
+    with torch.cuda.device(device):
+        _check(name, fn(*args, _stream(device)))
 
 
 def _workspace(t, nbytes: int, device):
@@ -146,9 +166,8 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
         fn, name = lib.fa_fwd_f32, "fa_fwd_f32"
     else:
         raise ValueError("dtype must be bfloat16 or float32")
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)), _stream(q.device))
-    _check(name, st)
+    _launch(name, fn, q.device, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)))
     return out, lse
 
 
@@ -167,11 +186,9 @@ def fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float,
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out = _buf(out, (B, Hq, Nq, d), torch.bfloat16, q8.device, "out")
     lse = _buf(lse, (B, Hq, Nq), torch.float32, q8.device, "lse")
-    st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
-                        lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc, float(descale_q),
-                        float(descale_k), float(descale_v), int(bool(causal)),
-                        _stream(q8.device))
-    _check("fa_fwd_fp8", st)
+    _launch("fa_fwd_fp8", lib.fa_fwd_fp8, q8.device, q8.data_ptr(), k8.data_ptr(),
+            v8.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc,
+            float(descale_q), float(descale_k), float(descale_v), int(bool(causal)))
     return out, lse
 
 
@@ -198,10 +215,9 @@ def fwd_variant(q, k, v, variant, causal: bool = False, scale: Optional[float] =
         workspace = _workspace(workspace, nbytes, q.device)
     wptr = workspace.data_ptr() if workspace is not None else None
     wlen = workspace.numel() if workspace is not None else 0
-    st = lib.fa_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), wptr, wlen, B, Hq, Hkv, Nq, Nk, d, sc,
-                            int(bool(causal)), var, _stream(q.device))
-    _check("fa_fwd_variant", st)
+    _launch("fa_fwd_variant", lib.fa_fwd_variant, q.device, q.data_ptr(), k.data_ptr(),
+            v.data_ptr(), out.data_ptr(), lse.data_ptr(), wptr, wlen, B, Hq, Hkv, Nq, Nk,
+            d, sc, int(bool(causal)), var)
     return out, lse
 
 
@@ -226,11 +242,9 @@ def fwd_splitkv(q, k, v, causal: bool = True, scale: Optional[float] = None,
     lse = _buf(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     nbytes = lib.fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
     workspace = _workspace(workspace, nbytes, q.device)
-    st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)),
-                            int(num_splits), workspace.data_ptr(), workspace.numel(),
-                            _stream(q.device))
-    _check("fa_fwd_splitkv", st)
+    _launch("fa_fwd_splitkv", lib.fa_fwd_splitkv, q.device, q.data_ptr(), k.data_ptr(),
+            v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc,
+            int(bool(causal)), int(num_splits), workspace.data_ptr(), workspace.numel())
     return out, lse
 
 
@@ -248,9 +262,9 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     lib = load()
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = _buf(o, q.shape, q.dtype, q.device, "o")
-    do = _buf(do, q.shape, q.dtype, q.device, "do")
-    lse = _buf(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
+    o = _inp(o, q.shape, q.dtype, q.device, "o")
+    do = _inp(do, q.shape, q.dtype, q.device, "do")
+    lse = _inp(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     dq = _buf(dq, q.shape, q.dtype, q.device, "dq")
     dk = _buf(dk, k.shape, k.dtype, k.device, "dk")
     dv = _buf(dv, v.shape, v.dtype, v.device, "dv")
@@ -259,9 +273,9 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, Nq, Nk, d, sc,
-            int(bool(causal)), _stream(q.device))
+            int(bool(causal)))
     if stage == -1:
-        _check("fa_bwd", lib.fa_bwd(*args))
+        _launch("fa_bwd", lib.fa_bwd, q.device, *args)
     else:
-        _check("fa_bwd_stage", lib.fa_bwd_stage(int(stage), *args))
+        _launch("fa_bwd_stage", lib.fa_bwd_stage, q.device, int(stage), *args)
     return dq, dk, dv

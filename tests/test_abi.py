@@ -182,3 +182,17 @@ def test_binding_rejects_wrong_output_buffers():
     assert fa._buf(t, (2, 4), torch.float32, dev, "out") is t
     with pytest.raises(ValueError):
         fa._workspace(torch.empty(16, dtype=torch.float32), 16, dev)
+
+
+def test_binding_requires_backward_inputs():
+    """O, dO and LSE are read by the backward: the binding never allocates them."""
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cpu")
+    with pytest.raises(ValueError):
+        fa._inp(None, (2, 4), torch.float32, dev, "o")
+    with pytest.raises(ValueError):
+        fa._inp(torch.empty(2, 4, dtype=torch.bfloat16), (2, 4), torch.float32, dev, "lse")
+    with pytest.raises(ValueError):
+        fa._inp(torch.empty(4, 2).t(), (2, 4), torch.float32, dev, "do")
+    t = torch.empty(2, 4)
+    assert fa._inp(t, (2, 4), torch.float32, dev, "o") is t
