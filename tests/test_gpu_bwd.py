@@ -52,6 +52,19 @@ def test_bwd_shapes(gpu_lib, shape):
     check(gpu_lib, inp, f"bwd{shape}")
 
 
+@pytest.mark.parametrize("shape", [
+    # at least 256 workgroups of 256 query rows: the 8-wave dQ kernel, ragged tails
+    (2, 32, 8, 1000, 1000, 128, True),
+    (2, 32, 16, 1024, 1100, 64, False),
+])
+def test_bwd_large_grid_shapes(gpu_lib, shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    assert -(-Nq // 256) * Hq * B >= 256
+    inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, with_do=True,
+                            seed=3200 + Nq + Nk + d)
+    check(gpu_lib, inp, f"bwd-large{shape}")
+
+
 def test_bwd_large_logits(gpu_lib):
     inp = synth.make_inputs(1, 4, 4, 512, 512, 64, causal=True, with_do=True, seed=3100,
                             q_mult=4.0)

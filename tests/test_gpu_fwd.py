@@ -63,6 +63,24 @@ def test_edge_shapes_bf16(gpu_lib, shape):
     check_full(gpu_lib, inp, f"edge{shape}")
 
 
+# Grids of at least 256 workgroups of 256 query rows run the 8-wave kernel; the shapes
+# above are small enough to take the 4-wave (128-row) one. These give the 8-wave
+# kernel ragged key tails, GQA and both causal alignments, compared element by element.
+LARGE_GRID = [
+    (2, 32, 8, 1000, 1000, 128, True),
+    (2, 32, 4, 1000, 1300, 64, True),       # Nk > Nq: bottom-right diagonal
+    (2, 32, 32, 1100, 700, 128, False),     # Nq > Nk, non-causal
+]
+
+
+@pytest.mark.parametrize("shape", LARGE_GRID)
+def test_large_grid_shapes_bf16(gpu_lib, shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    assert -(-Nq // 256) * Hq * B >= 256
+    inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, seed=1500 + Nq + Nk + d)
+    check_full(gpu_lib, inp, f"large{shape}")
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 1, 70, 90, 4, True), (1, 1, 1, 33, 33, 20, False),
                                    (2, 4, 2, 129, 129, 128, True), (1, 1, 1, 5, 300, 256, False)])
 def test_edge_shapes_fp32(gpu_lib, shape):
