@@ -9,7 +9,9 @@ the forward, 2.5x that for the backward, halved for causal.
 Prints one JSON line. Besides the headline value it carries:
   roofline      the dominant kernel's algorithmic FLOP/s (HIP events on the launch
                 stream) against the bf16 dense MFMA peak, plus its HBM traffic when a
-                counter summary for the current kernel source is in profiles/;
+                counter summary for the current kernel source is in profiles/, and
+                the matrix-core rate measured on this GPU (fa_mfma_probe, zeros and
+                normal-like bf16 operands) with the kernel's fraction of the latter;
   cpu_baseline  the float64 oracle on this host, timed on a bounded sample;
   phases        per-kernel average milliseconds;
   extra         forward/decode throughput of the other workloads (fewer iterations).
@@ -151,6 +153,24 @@ def timed_ms(torch, call, iters, warm_ms=50.0):
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters
+
+
+def mfma_ceiling(torch, fa, blocks=4096, iters=400, reps=5):
+    """Measured matrix-core rate (fa_mfma_probe): bf16 32x32x16 products on register
+    operands that are zeros or normal-like bf16, in TFLOP/s. The chip's clock under
+    matrix load depends on the operand bits, so the normal-like figure is the ceiling
+    a dense bf16 product on this workload's data can reach on this GPU."""
+    res = {}
+    out = torch.empty(blocks * 256, device="cuda", dtype=torch.float32)
+    for kind in ("zeros", "normal_bf16"):
+        flop = [0.0]
+
+        def call():
+            flop[0], _ = fa.mfma_probe(blocks, iters, kind, out=out)
+        ms = timed_ms(torch, call, reps)
+        res[kind] = round(flop[0] / ms / 1e9, 1)
+    del out
+    return res
 
 
 def extras(torch, fa, iters=20):
@@ -380,6 +400,11 @@ def main():
                          "bwd": round(2.5 * f_fwd / (ms["bwd_pre_kernel"] + ms["bwd_dkdv_kernel"]
                                                      + ms["bwd_dq_kernel"]) / 1e9, 1)},
     }
+    if not args.profile:
+        log("matrix-core ceiling")
+        ceil = mfma_ceiling(torch, fa)
+        roofline["measured_mfma_tflops"] = ceil
+        roofline["frac_of_measured_normal_bf16"] = round(achieved / ceil["normal_bf16"], 4)
     if not args.profile and not args.no_extra:
         log("extra workloads")
         rec["extra"] = extras(torch, fa)

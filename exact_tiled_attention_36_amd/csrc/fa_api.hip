@@ -234,4 +234,13 @@ int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* 
                                          (float*)workspace, s, (hipStream_t)stream));
 }
 
+int fa_mfma_probe(float* out, int blocks, int iters, int kind, void* stream) {
+  if (!out) return FA_ERR_NULL;
+  if (!aligned16(out)) return FA_ERR_ALIGN;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20) ||
+      (kind != 0 && kind != 1))
+    return FA_ERR_SHAPE;
+  return launch_status(fa::launch_mfma_probe(out, blocks, iters, kind, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -52,4 +52,9 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec,
                       const AttnShape& s, int stage, hipStream_t st);
 
+// Matrix-core rate probe: `blocks` workgroups of 256 threads, each wave running
+// iters x 16 bf16 32x32x16 products on register operands (kind 0 zeros, 1 normal-like
+// bf16); one float per thread is written to out (blocks * 256 floats).
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, int kind, hipStream_t st);
+
 }  // namespace fa

@@ -41,6 +41,7 @@ _SIGNATURES = {
     "fa_fwd_variant_workspace_bytes": (_c_size, [_c_int] * 7),
     "fa_fwd_variant": (_c_int, [_vp] * 6 + [_c_size] + [_c_int] * 6
                        + [_c_float, _c_int, _c_int, _vp]),
+    "fa_mfma_probe": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -279,3 +280,20 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     else:
         _launch("fa_bwd_stage", lib.fa_bwd_stage, q.device, int(stage), *args)
     return dq, dk, dv
+
+
+MFMA_PROBE_KINDS = {"zeros": 0, "normal_bf16": 1}
+
+
+def mfma_probe(blocks: int, iters: int, kind="normal_bf16", device=None, out=None):
+    """Enqueue fa_mfma_probe on the current stream of `device` (a measurement helper:
+    blocks * 4 waves, each iters * 16 bf16 32x32x16 matrix products on register
+    operands, zeros or normal-like bf16). Returns (flop, out); time the call with
+    events on the same stream."""
+    import torch
+    lib = load()
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    k = MFMA_PROBE_KINDS[kind] if isinstance(kind, str) else int(kind)
+    out = _buf(out, (int(blocks) * 256,), torch.float32, dev, "out")
+    _launch("fa_mfma_probe", lib.fa_mfma_probe, dev, out.data_ptr(), int(blocks), int(iters), k)
+    return float(blocks) * 4 * iters * 16 * 32768, out

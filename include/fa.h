@@ -192,6 +192,23 @@ int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* 
                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
                    int Nk, int d, float scale, int causal, int variant, void* stream);
 
+/*
+ * fa_mfma_probe — measurement helper (not part of the attention computation): the
+ * sustained rate of the bf16 matrix instruction the kernels use
+ * (v_mfma_f32_32x32x16_bf16), so that a kernel's achieved TFLOP/s can be read
+ * against what the matrix cores deliver at the clock the chip actually runs.
+ * Launches `blocks` workgroups of 256 threads; every wave runs iters x 16 products
+ * (32*32*16*2 flop each) on operands held in registers: kind 0 fills them with
+ * zeros, kind 1 with bf16 values drawn from an approximately standard normal
+ * distribution (the attention workloads' input distribution; the chip's clock under
+ * matrix load depends on the operand bits). Total work: blocks * 4 * iters * 16 *
+ * 32768 flop; the caller times the call (e.g. with events on `stream`).
+ * out: device buffer of blocks * 256 floats (written, values meaningless), 16-byte
+ * aligned. Errors: FA_ERR_NULL, FA_ERR_ALIGN, FA_ERR_SHAPE (blocks not in
+ * [1, 1 << 20], iters not in [1, 1 << 20], kind not 0 or 1), FA_ERR_LAUNCH.
+ */
+int fa_mfma_probe(float* out, int blocks, int iters, int kind, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

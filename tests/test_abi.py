@@ -196,3 +196,11 @@ def test_binding_requires_backward_inputs():
         fa._inp(torch.empty(4, 2).t(), (2, 4), torch.float32, dev, "do")
     t = torch.empty(2, 4)
     assert fa._inp(t, (2, 4), torch.float32, dev, "o") is t
+
+
+def test_mfma_probe_validation(lib):
+    assert lib.fa_mfma_probe(NULL, 1, 1, 0, None) == -1
+    assert lib.fa_mfma_probe(PU, 1, 1, 0, None) == -5
+    for blocks, iters, kind in ((0, 1, 0), (1, 0, 0), (1 << 21, 1, 0), (1, 1 << 21, 0),
+                                (1, 1, 2), (1, 1, -1)):
+        assert lib.fa_mfma_probe(P, blocks, iters, kind, None) == -2, (blocks, iters, kind)
