@@ -118,8 +118,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int kb = L % nkb, bkv = L / nkb;
+  // key block kb is seen by the most query rows at kb = 0
+  int kb, bkv;
+  if (CAUSAL) {
+    causal_order(blockIdx.x, gridDim.x, nkb, bkv, kb);
+    kb = nkb - 1 - kb;
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    kb = L % nkb;
+    bkv = L / nkb;
+  }
   const int kvh = bkv % p.Hkv, b = bkv / p.Hkv;
   const int k0 = kb * BNK;
   const int key = k0 + 32 * w + l32;
@@ -512,9 +520,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  int qb = L % nqb;
-  const int bh = L / nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;
+  int qb, bh;
+  if (CAUSAL) {
+    causal_order(blockIdx.x, gridDim.x, nqb, bh, qb);
+  } else {
+    qb = L % nqb;
+    bh = L / nqb;
+  }
   const int h = bh % p.Hq, b = bh / p.Hq, kvh = h / p.g;
   const int q0 = qb * BM;
   const int w0 = q0 + 32 * wu;

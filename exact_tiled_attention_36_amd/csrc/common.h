@@ -359,4 +359,30 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// (batch*head, row block) of workgroup `hw` of a causal launch of n = nbh * nqb
+// workgroups, longest row blocks (the last ones, which see the most keys) first.
+// Workgroup hw runs on XCD hw % 8 as the (hw / 8)-th of that XCD.
+//  * nbh a multiple of 8: each XCD owns nbh / 8 whole (batch, head) pairs (their K/V
+//    stay in its L2) and takes their row blocks two heads at a time, alternating
+//    between the two from the longest down. One head at a time would leave the long
+//    blocks of an XCD's last head to start when most compute units are already
+//    finishing short ones.
+//  * otherwise a head's blocks cannot stay on one XCD without giving some XCDs only
+//    long blocks and others only short ones: ids run over every head at one
+//    row-block level, longest level first, so each XCD gets the same mix.
+__device__ __forceinline__ void causal_order(int hw, int n, int nqb, int& bh, int& qb) {
+  const int nbh = n / nqb;
+  if ((nbh & 7) == 0) {
+    const int k = nbh >> 3, x = hw & 7, slot = hw >> 3;
+    const int pair = slot / (2 * nqb);
+    const int nh = min(2, k - 2 * pair);
+    const int r = slot - pair * 2 * nqb;
+    bh = x * k + 2 * pair + (nh == 2 ? (r & 1) : 0);
+    qb = nqb - 1 - (nh == 2 ? (r >> 1) : r);
+  } else {
+    bh = hw % nbh;
+    qb = nqb - 1 - hw / nbh;
+  }
+}
+
 }  // namespace fa

@@ -148,9 +148,13 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_fp8_kernel(Fp8Params p) {
   const int l32 = lane & 31, hi = lane >> 5;
 
   int L = xcd_remap(blockIdx.x, gridDim.x);
-  int qb = L % p.nqb;
-  const int bh = L / p.nqb;
-  if (CAUSAL) qb = p.nqb - 1 - qb;
+  int qb, bh;
+  if (CAUSAL) {
+    causal_order(blockIdx.x, gridDim.x, p.nqb, bh, qb);
+  } else {
+    qb = L % p.nqb;
+    bh = L / p.nqb;
+  }
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.g;
   const int q0 = qb * BM;

@@ -57,7 +57,8 @@ def load(path: Optional[str] = None, require_torch: bool = True):
     """Load libfa.so once and attach the C signatures. Raises if it is not built.
 
     The library next to this file is used unless ``path`` or the environment variable
-    FA_LIBRARY names another build of the same sources."""
+    FA_LIBRARY names another build of the same sources. The library loaded last is
+    the one every call of this module uses."""
     global _lib
     if _lib is not None and path is None:
         return _lib
@@ -72,8 +73,7 @@ def load(path: Optional[str] = None, require_torch: bool = True):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if path is None:
-        _lib = lib
+    _lib = lib
     return lib
 
 
