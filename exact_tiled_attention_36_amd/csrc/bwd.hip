@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   // key block kb is seen by the most query rows at kb = 0
   int kb, bkv;
   if (CAUSAL) {
-    causal_order(blockIdx.x, gridDim.x, nkb, bkv, kb);
+    causal_order<1>(blockIdx.x, gridDim.x, nkb, bkv, kb);
     kb = nkb - 1 - kb;
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int qb, bh;
   if (CAUSAL) {
-    causal_order(blockIdx.x, gridDim.x, nqb, bh, qb);
+    causal_order<2>(blockIdx.x, gridDim.x, nqb, bh, qb);
   } else {
     qb = L % nqb;
     bh = L / nqb;

@@ -363,21 +363,25 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
 // workgroups, longest row blocks (the last ones, which see the most keys) first.
 // Workgroup hw runs on XCD hw % 8 as the (hw / 8)-th of that XCD.
 //  * nbh a multiple of 8: each XCD owns nbh / 8 whole (batch, head) pairs (their K/V
-//    stay in its L2) and takes their row blocks two heads at a time, alternating
-//    between the two from the longest down. One head at a time would leave the long
-//    blocks of an XCD's last head to start when most compute units are already
-//    finishing short ones.
+//    stay in its L2) and takes their row blocks C heads at a time, alternating
+//    between them from the longest down. With C = 1 the long blocks of an XCD's last
+//    head start when most compute units are already finishing short ones (about 9 %
+//    of tail at 16 row blocks per head); C = 2 hands them out in the first half. A
+//    kernel whose concurrent workgroups share tiles of one head in L2 (dK/dV) keeps
+//    C = 1.
 //  * otherwise a head's blocks cannot stay on one XCD without giving some XCDs only
 //    long blocks and others only short ones: ids run over every head at one
 //    row-block level, longest level first, so each XCD gets the same mix.
+template <int C>
 __device__ __forceinline__ void causal_order(int hw, int n, int nqb, int& bh, int& qb) {
+  static_assert(C == 1 || C == 2, "one or two heads at a time");
   const int nbh = n / nqb;
   if ((nbh & 7) == 0) {
     const int k = nbh >> 3, x = hw & 7, slot = hw >> 3;
-    const int pair = slot / (2 * nqb);
-    const int nh = min(2, k - 2 * pair);
-    const int r = slot - pair * 2 * nqb;
-    bh = x * k + 2 * pair + (nh == 2 ? (r & 1) : 0);
+    const int pair = slot / (C * nqb);
+    const int nh = min(C, k - C * pair);
+    const int r = slot - pair * C * nqb;
+    bh = x * k + C * pair + (nh == 2 ? (r & 1) : 0);
     qb = nqb - 1 - (nh == 2 ? (r >> 1) : r);
   } else {
     bh = hw % nbh;

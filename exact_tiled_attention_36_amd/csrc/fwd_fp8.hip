@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_fp8_kernel(Fp8Params p) {
   int L = xcd_remap(blockIdx.x, gridDim.x);
   int qb, bh;
   if (CAUSAL) {
-    causal_order(blockIdx.x, gridDim.x, p.nqb, bh, qb);
+    causal_order<2>(blockIdx.x, gridDim.x, p.nqb, bh, qb);
   } else {
     qb = L % p.nqb;
     bh = L / p.nqb;
