@@ -56,6 +56,10 @@ def test_bwd_shapes(gpu_lib, shape):
     # at least 256 workgroups of 256 query rows: the 8-wave dQ kernel, ragged tails
     (2, 32, 8, 1000, 1000, 128, True),
     (2, 32, 16, 1024, 1100, 64, False),
+    # causal orders: dQ over 72 (batch, head) pairs (9 per XCD), dK/dV over 24 kv
+    # pairs (3 per XCD); then 68 and 17 pairs, which do not split evenly over 8 XCDs
+    (3, 24, 8, 1000, 1000, 128, True),
+    (1, 68, 17, 1000, 1000, 64, True),
 ])
 def test_bwd_large_grid_shapes(gpu_lib, shape):
     B, Hq, Hkv, Nq, Nk, d, causal = shape

@@ -70,6 +70,10 @@ LARGE_GRID = [
     (2, 32, 8, 1000, 1000, 128, True),
     (2, 32, 4, 1000, 1300, 64, True),       # Nk > Nq: bottom-right diagonal
     (2, 32, 32, 1100, 700, 128, False),     # Nq > Nk, non-causal
+    # causal row-block orders: 72 (batch, head) pairs = 9 per XCD (pairs of heads and
+    # one head alone); 68 pairs do not split evenly over 8 XCDs (level-major order)
+    (3, 24, 8, 1000, 1000, 128, True),
+    (1, 68, 17, 1000, 1000, 64, True),
 ]
 
 
