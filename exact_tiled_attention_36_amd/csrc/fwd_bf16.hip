@@ -32,8 +32,10 @@
 //    another wave on the same SIMD). K runs two tiles ahead of V in the LDS buffers.
 //  * tiles that no row of the workgroup needs masked for (causal diagonal, key tail)
 //    run in a loop without mask code; the rest in a masked loop.
-//  * grid: one workgroup per (batch, head, row block), ids remapped so consecutive
-//    ids stay on one XCD (one L2) and, for causal, the longest row blocks go first.
+//  * grid: one workgroup per (batch, head, row block). Non-causal ids are remapped so
+//    consecutive ids stay on one XCD (one L2); causal grids follow causal_order: the
+//    longest row blocks first, balanced over the 8 XCDs, two heads interleaved per
+//    XCD.
 #include "common.h"
 #include "kernels.h"
 
