@@ -17,7 +17,8 @@ Prints one JSON line. Besides the headline value it carries:
   extra         forward/decode throughput of the other workloads (fewer iterations).
 
 Modes: default; --profile (no oracle/extras, a known-size copy first, for rocprofv3
-counter runs that calibrate FETCH_SIZE/WRITE_SIZE).
+counter runs that calibrate FETCH_SIZE/WRITE_SIZE; after the step, short runs of the
+matrix-core probe, the d=64 forward and both decode shapes).
 """
 import argparse
 import hashlib
@@ -301,6 +302,30 @@ def version_ablation(torch, fa, g, iters=5, reps=5):
     return res
 
 
+def profile_tail(torch, fa, calls=3):
+    """Counter-run mode only: short runs of the kernels outside the training step, so one
+    rocprofv3 pass also covers them: fa_mfma_probe on normal-like bf16 operands (matrix
+    cores busy by construction: the reference for the busy-cycle counter), the
+    non-causal B2 H16 N1024 d64 forward, and split-KV decode at B8 H8 Nk32768 d128 (one
+    row per kv-head) and B16 Hq32 Hkv4 Nk8192 d128 (eight rows)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    out = torch.empty(1024 * 256, device="cuda", dtype=torch.float32)
+    for _ in range(calls):
+        fa.mfma_probe(1024, 200, "normal_bf16", out=out)
+    rnd = lambda *shape: torch.randn(*shape, device="cuda", dtype=torch.bfloat16, generator=g)
+    q, k, v = rnd(2, 16, 1024, 64), rnd(2, 16, 1024, 64), rnd(2, 16, 1024, 64)
+    for _ in range(calls):
+        fa.fwd(q, k, v, causal=False)
+    for B, Hq, Hkv, Nk in ((8, 8, 8, 32768), (16, 32, 4, 8192)):
+        q, k, v = rnd(B, Hq, 1, 128), rnd(B, Hkv, Nk, 128), rnd(B, Hkv, Nk, 128)
+        ws = torch.empty(fa.splitkv_workspace_bytes(B, Hq, Hkv, 1, Nk, 128), device="cuda",
+                         dtype=torch.uint8)
+        for _ in range(calls):
+            fa.fwd_splitkv(q, k, v, causal=True, workspace=ws)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,7 +334,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="counter-run mode: 1 GiB copy first, no oracle, no extras")
+                    help="counter-run mode: 1 GiB copy first, then the step; afterwards three "
+                         "calls each of the matrix-core probe, the d=64 forward and the two "
+                         "decode shapes; no oracle, no extras")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -400,6 +427,8 @@ def main():
                          "bwd": round(2.5 * f_fwd / (ms["bwd_pre_kernel"] + ms["bwd_dkdv_kernel"]
                                                      + ms["bwd_dq_kernel"]) / 1e9, 1)},
     }
+    if args.profile:
+        profile_tail(torch, fa)
     if not args.profile:
         log("matrix-core ceiling")
         ceil = mfma_ceiling(torch, fa)
