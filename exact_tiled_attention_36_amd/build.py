@@ -26,6 +26,9 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
+# Options for single files: the d = 128 dK/dV kernel has its matrix products write
+# ordinary vector registers (see the file's header).
+FILE_FLAGS = {"bwd_dkdv_d128.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -37,7 +40,8 @@ def hipcc() -> str:
 
 def _compile(src: str, extra=(), tag: str = "") -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra,
+           "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

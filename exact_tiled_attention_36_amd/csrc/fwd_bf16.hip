@@ -432,7 +432,10 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 #endif
     case 64: return c ? run<64, FWD_CFG64, true>(p, s.B, st) : run<64, FWD_CFG64, false>(p, s.B, st);
     case 128: return c ? run<128, FWD_CFG128, true>(p, s.B, st) : run<128, FWD_CFG128, false>(p, s.B, st);
-    case 256: return c ? run<256, 32, 4, 1, true>(p, s.B, st) : run<256, 32, 4, 1, false>(p, s.B, st);
+#ifndef FWD_CFG256
+#define FWD_CFG256 32, 4, 1
+#endif
+    case 256: return c ? run<256, FWD_CFG256, true>(p, s.B, st) : run<256, FWD_CFG256, false>(p, s.B, st);
     default: return hipErrorInvalidValue;
   }
 }
