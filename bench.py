@@ -2,7 +2,7 @@
 
 One step = the whole hot path on one batch of the GQA training workload
 (B=2, Hq=32, Hkv=8, N=8192, d=128, causal, bf16): forward (fa_fwd) then the
-recompute backward (fa_bwd_stage 0, 1, 2 = D preprocess, dK/dV, dQ), with inputs
+recompute backward (fa_bwd_stage 0, 1 = dQ with the row statistics D, dK/dV), with inputs
 resident in HBM. FLOPs per step follow the method's accounting: 4*B*Hq*Nq*Nk*d for
 the forward, 2.5x that for the backward, halved for causal.
 
@@ -39,7 +39,6 @@ PEAK_HBM_GBS = 8000.0
 WORKLOAD = "c5_bf16_causal_gqa_B2Hq32Hkv8N8192d128"
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fwd_bf16.hip", "common.h"],
-    "bwd_pre_kernel": ["bwd.hip", "common.h"],
     "bwd_dkdv_kernel": ["bwd_dkdv.h", "bwd_dkdv_d128.hip", "bwd.hip", "common.h"],
     "bwd_dq_kernel": ["bwd.hip", "common.h"],
 }
@@ -381,7 +380,7 @@ def main():
         run = timer.mark if record else (lambda name, fn: fn())
         run("fwd_bf16_kernel", lambda: fa.fwd(q, k, v, causal=causal, scale=inp.scale,
                                               out=o, lse=lse))
-        for stg, name in ((0, "bwd_pre_kernel"), (1, "bwd_dkdv_kernel"), (2, "bwd_dq_kernel")):
+        for stg, name in ((0, "bwd_dq_kernel"), (1, "bwd_dkdv_kernel")):
             run(name, lambda stg=stg: fa.bwd(q, k, v, o, do, lse, causal=causal,
                                              scale=inp.scale, dq=dq, dk=dk, dv=dv,
                                              workspace=ws, stage=stg))
@@ -424,8 +423,8 @@ def main():
         "roofline": roofline,
         "phases_ms": {kname: round(t, 4) for kname, t in ms.items()},
         "phase_tflops": {"fwd": round(f_fwd / ms["fwd_bf16_kernel"] / 1e9, 1),
-                         "bwd": round(2.5 * f_fwd / (ms["bwd_pre_kernel"] + ms["bwd_dkdv_kernel"]
-                                                     + ms["bwd_dq_kernel"]) / 1e9, 1)},
+                         "bwd": round(2.5 * f_fwd / (ms["bwd_dkdv_kernel"] + ms["bwd_dq_kernel"])
+                                     / 1e9, 1)},
     }
     if args.profile:
         profile_tail(torch, fa)

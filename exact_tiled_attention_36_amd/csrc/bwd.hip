@@ -10,21 +10,22 @@
 //     dV   = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K
 // with dK, dV summed over the query heads that share a key/value head.
 //
-// Three kernels on one stream:
-//  1. bwd_pre:  D for every query row (HBM-bound row dot products).
-//  2. bwd_dkdv (bwd_dkdv.h): one workgroup per (batch, kv-head, 128 keys); each wave keeps 32 keys
-//     of K and V in registers and loops over the group's query heads and the query
-//     blocks that can see its keys (diagonal blocks first, then the unmasked ones
-//     block by block from the last down, all heads of the group per block, so the
+// Two kernels on one stream:
+//  1. bwd_dq (first): one workgroup per (batch, head, 32 queries per wave: 256 at
+//     d <= 128, 128 at d = 256); Q and dO stay in registers, K/V tiles are triple
+//     buffered in LDS; S^T and dP^T put one query per lane, so LSE and D are per-lane
+//     scalars, and dQ^T += K^T dS^T reads K^T with LDS transpose loads. Its prologue
+//     forms D_i from its rows of O and dO (dO is in registers already) and stores D
+//     and LSE * log2(e) for the second kernel.
+//  2. bwd_dkdv (bwd_dkdv.h): one workgroup per (batch, kv-head, 128 keys); each wave
+//     keeps 32 keys of K and V in registers and loops over the group's query heads and
+//     the query blocks that can see its keys (diagonal blocks first, then the unmasked
+//     ones block by block from the last down, all heads of the group per block, so the
 //     group's waves share Q/dO tiles in L2), with Q/dO/LSE/D tiles triple buffered in
 //     LDS.
 //     S = Q K^T and dP = dO V^T come out with one key per lane, so P and dS (rounded
 //     to bf16) feed dV^T += dO^T P and dK^T += Q^T dS directly as B operands; dO^T
 //     and Q^T are read with LDS transpose loads.
-//  3. bwd_dq:   one workgroup per (batch, head, 32 queries per wave: 256 at d <= 128,
-//     128 at d = 256); Q and dO stay in registers, K/V tiles are triple buffered in
-//     LDS; S^T and dP^T put one query per lane, so LSE and D are per-lane scalars, and
-//     dQ^T += K^T dS^T reads K^T with LDS transpose loads.
 // No atomics: every output element is written by exactly one workgroup, so results
 // are bitwise reproducible.
 #include "bwd_dkdv.h"
@@ -33,34 +34,7 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------------
-// 1. D_i = sum_c dO_ic * O_ic
-// ---------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int rows) {
-  constexpr int LPR = D / 8;        // lanes per row, 8 elements (16 bytes) each
-  constexpr int RPB = 256 / LPR;    // rows per workgroup pass
-  const int tid = threadIdx.x, sub = tid % LPR;
-  for (int row = blockIdx.x * RPB + tid / LPR; row < rows; row += gridDim.x * RPB) {
-    const u32x4_t a = ((const u32x4_t*)(p.o + (size_t)row * D))[sub];
-    const u32x4_t b = ((const u32x4_t*)(p.dO + (size_t)row * D))[sub];
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
-      acc = fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
-    }
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-    if (sub == 0) {
-      p.dvec[row] = acc;
-      const float l = p.lse[row];
-      p.lse2v[row] = l == -INFINITY ? INFINITY : l * kLog2e;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// 3. dQ
+// 1. dQ, with D
 // ---------------------------------------------------------------------------------
 // One workgroup = NW waves x 32 query rows; Q and dO stay in registers, each wave
 // owns its rows' dQ. Key tiles of BN rows (K and V) are triple buffered in LDS and
@@ -109,8 +83,31 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
       doreg[dc] = __builtin_bit_cast(bf16x8_t, os[2 * dc]);
     }
   }
-  const float lse2 = qvalid ? p.lse2v[rowidx] : INFINITY;
-  const float Dv = qvalid ? p.dvec[rowidx] : 0.f;
+  // D_i = sum_c dO_ic O_ic: this lane's half of the row of O, read in the layout of
+  // dO, then the two halves combined. D and LSE * log2(e) also go to the workspace
+  // for the dK/dV kernel.
+  float dpart = 0.f;
+  {
+    const u32x4_t* os = (const u32x4_t*)(p.o + rowidx * D + 8 * hi);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      const u32x4_t ov = os[2 * dc];
+      const u32x4_t dv = __builtin_bit_cast(u32x4_t, doreg[dc]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dpart = fmaf(bf16_lo(ov[i]), bf16_lo(dv[i]), dpart);
+        dpart = fmaf(bf16_hi(ov[i]), bf16_hi(dv[i]), dpart);
+      }
+    }
+  }
+  const float dsum = xhalf_sum(dpart);
+  const float lraw = p.lse[rowidx];
+  const float Dv = qvalid ? dsum : 0.f;
+  const float lse2 = (!qvalid || lraw == -INFINITY) ? INFINITY : lraw * kLog2e;
+  if (qvalid && hi == 0) {
+    p.dvec[rowidx] = Dv;
+    p.lse2v[rowidx] = lse2;
+  }
   // nothing may be outstanding in the loops below except the tile copies they issue
   wait_vmem();
 
@@ -277,15 +274,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   }
 }
 
-// stage 0: D = rowsum(dO * O); stage 1: dK, dV; stage 2: dQ; stage -1: all three.
+// stage 0: dQ (and D, LSE * log2(e) into the workspace); stage 1: dK, dV; stage -1: both.
 template <int D, int BMQ, int BN, int NWQ, bool CAUSAL>
 hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
   if (stage == -1 || stage == 0) {
-    const int rows = B * p.Hq * p.Nq;
-    constexpr int RPB = 256 / (D / 8);
-    int nb = (rows + RPB - 1) / RPB;
-    if (nb > 65536) nb = 65536;
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(nb), dim3(256), 0, st, p, rows);
+    const int nqb = (p.Nq + 32 * NWQ - 1) / (32 * NWQ);
+    const long long n = (long long)nqb * p.Hq * B;
+    if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, NWQ, CAUSAL>), dim3((int)n), dim3(64 * NWQ), 0, st, p, nqb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -300,14 +296,6 @@ hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, BMQ, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nkb);
       e = hipGetLastError();
     }
-    if (e != hipSuccess) return e;
-  }
-  if (stage == -1 || stage == 2) {
-    const int nqb = (p.Nq + 32 * NWQ - 1) / (32 * NWQ);
-    const long long n = (long long)nqb * p.Hq * B;
-    if (n > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, NWQ, CAUSAL>), dim3((int)n), dim3(64 * NWQ), 0, st, p, nqb);
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

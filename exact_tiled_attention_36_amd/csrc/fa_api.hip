@@ -66,7 +66,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: problem exceeds the library's index range";
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits out of range";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale (and every FP8 descale) must be finite and > 0";
-    case FA_ERR_STAGE: return "FA_ERR_STAGE: backward stage must be 0, 1 or 2";
+    case FA_ERR_STAGE: return "FA_ERR_STAGE: backward stage must be 0 or 1";
     case FA_ERR_VARIANT: return "FA_ERR_VARIANT: forward variant must be 0, 1, 2 or 3";
     default: return "unknown fa status code";
   }
@@ -198,7 +198,7 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const void* dO, const float* lse, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
                  int Nk, int d, float scale, int causal, void* stream) {
-  if (stage < 0 || stage > 2) return FA_ERR_STAGE;
+  if (stage < 0 || stage > 1) return FA_ERR_STAGE;
   return bwd_common(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
                     Nq, Nk, d, scale, causal, stage, stream);
 }

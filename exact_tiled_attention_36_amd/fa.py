@@ -257,8 +257,8 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
         dq=None, dk=None, dv=None, workspace=None, stage: int = -1):
     """dQ, dK, dV (bf16) by recomputation from the forward's O and LSE.
 
-    ``stage`` -1 runs the whole backward (fa_bwd); 0, 1, 2 run one kernel stage
-    (fa_bwd_stage: D preprocess, dK/dV, dQ) with the same buffers."""
+    ``stage`` -1 runs the whole backward (fa_bwd); 0, 1 run one kernel stage
+    (fa_bwd_stage: dQ with the row statistics D, then dK/dV) with the same buffers."""
     import torch
     lib = load()
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)

@@ -59,7 +59,7 @@ enum {
   FA_ERR_TOO_LARGE = -8,  /* an index would overflow 32/64-bit addressing limits */
   FA_ERR_SPLITS = -9,     /* num_splits out of range                             */
   FA_ERR_SCALE = -10,     /* scale (or an FP8 descale) is not a finite number > 0 */
-  FA_ERR_STAGE = -11,     /* fa_bwd_stage: stage not in {0, 1, 2}                */
+  FA_ERR_STAGE = -11,     /* fa_bwd_stage: stage not in {0, 1}                   */
   FA_ERR_VARIANT = -12    /* fa_fwd_variant: variant not in {0, 1, 2, 3}         */
 };
 
@@ -151,11 +151,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 /*
  * One stage of fa_bwd, same arguments plus `stage`, for callers that schedule or
- * time the three kernels separately. fa_bwd == stage 0, then 1, then 2 on one stream.
- *   stage 0: D_i = sum_c dO_ic o_ic into the workspace (must run first);
- *   stage 1: dk and dv (reads D);
- *   stage 2: dq (reads D).
- * Stages 1 and 2 are independent of each other. Returns FA_ERR_STAGE for other values.
+ * time the two kernels separately. fa_bwd == stage 0, then 1 on one stream.
+ *   stage 0: dq, and D_i = sum_c dO_ic o_ic and a log2-scaled copy of lse into the
+ *            workspace (must run first);
+ *   stage 1: dk and dv (reads both from the workspace).
+ * Returns FA_ERR_STAGE for other values.
  */
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const void* dO, const float* lse, void* dq, void* dk, void* dv,

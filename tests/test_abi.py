@@ -118,7 +118,7 @@ def test_bwd_validation_and_workspace(lib):
 def test_bwd_stage_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 1, 8, 8, 128)
     args = [P] * 9 + [P, ws, 1, 2, 1, 8, 8, 128, 0.1, 1, None]
-    for stage in (-2, 3, 7):
+    for stage in (-2, 2, 3, 7):
         assert lib.fa_bwd_stage(stage, *args) == -11, stage
     assert lib.fa_bwd_stage(0, *([NULL] + [P] * 8 + [P, ws, 1, 2, 1, 8, 8, 128, 0.1, 1, None])) == -1
 
