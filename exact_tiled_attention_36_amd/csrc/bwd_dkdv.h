@@ -275,7 +275,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   };
 
   // MASK: the step touches the causal diagonal or reaches past the last query row.
-  auto step = [&](auto mask_tag, int s, int i0) FA_INLINE {
+  // issue_next: the copies of the next step's tiles, issued right behind the step's
+  // first operand reads, so their address work overlaps the reads' latency (issued
+  // before the reads, after the barrier, they delayed the step's first products)
+  auto step = [&](auto mask_tag, int s, int i0, auto&& issue_next) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* Qs = qtile(s);
     const uint16_t* Qp = s > 0 ? qtile(s - 1) : Qs;  // with P = dS = 0 at s = 0
@@ -356,6 +359,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     };
 
     rd_s(0, 0);
+    issue_next();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
@@ -399,22 +403,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   }
   __syncthreads();
 
-  // Step s copies the tiles of step s+1 into buffer (s+1)%3 first (tiles of the
-  // unmasked loop lie wholly below Nq). cur positions step s, nxt step s+1.
+  // Step s copies the tiles of step s+1 into buffer (s+1)%3, behind its own first
+  // operand reads (tiles of the unmasked loop lie wholly below Nq). cur positions step
+  // s, nxt step s+1.
   Cur nxt = cur;
   cur_next(nxt);
   int s = 0;
   for (; s < total_m; ++s) {
-    if (s + 1 < total) issue_at(s + 1, pos_of(nxt));
-    step(BoolC<true>(), s, cur_i0(cur));
+    step(BoolC<true>(), s, cur_i0(cur), [&]() FA_INLINE {
+      if (s + 1 < total) issue_at(s + 1, pos_of(nxt));
+    });
     cur = nxt;
     cur_next(nxt);
     wait_vmem();
     __syncthreads();
   }
   for (; s < total; ++s) {
-    if (s + 1 < total) issue_full(s + 1, pos_of(nxt));
-    step(BoolC<false>(), s, cur_i0(cur));
+    step(BoolC<false>(), s, cur_i0(cur), [&]() FA_INLINE {
+      if (s + 1 < total) issue_full(s + 1, pos_of(nxt));
+    });
     cur = nxt;
     cur_next(nxt);
     wait_vmem();
