@@ -353,7 +353,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2). Map the
 // hardware id to a logical id so that consecutive logical ids run on one XCD.
-__device__ __forceinline__ int xcd_remap(int hw, int n) {
+__host__ __device__ __forceinline__ int xcd_remap(int hw, int n) {
   const int x = hw & 7, slot = hw >> 3;
   const int per = n >> 3, rem = n & 7;
   return x * per + (x < rem ? x : rem) + slot;
@@ -373,13 +373,14 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
 //    long blocks and others only short ones: ids run over every head at one
 //    row-block level, longest level first, so each XCD gets the same mix.
 template <int C>
-__device__ __forceinline__ void causal_order(int hw, int n, int nqb, int& bh, int& qb) {
+__host__ __device__ __forceinline__ void causal_order(int hw, int n, int nqb, int& bh,
+                                                      int& qb) {
   static_assert(C == 1 || C == 2, "one or two heads at a time");
   const int nbh = n / nqb;
   if ((nbh & 7) == 0) {
     const int k = nbh >> 3, x = hw & 7, slot = hw >> 3;
     const int pair = slot / (C * nqb);
-    const int nh = min(C, k - C * pair);
+    const int nh = C < k - C * pair ? C : k - C * pair;
     const int r = slot - pair * C * nqb;
     bh = x * k + C * pair + (nh == 2 ? (r & 1) : 0);
     qb = nqb - 1 - (nh == 2 ? (r >> 1) : r);
