@@ -38,7 +38,7 @@ PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 2.4 GHz x 8192 dense fp8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "c5_bf16_causal_gqa_B2Hq32Hkv8N8192d128"
 KERNEL_SOURCES = {
-    "fwd_bf16_kernel": ["fwd_bf16.hip", "common.h"],
+    "fwd_bf16_kernel": ["fwd_bf16.h", "fwd_bf16.hip", "common.h"],
     "bwd_dkdv_kernel": ["bwd_dkdv.h", "bwd_dkdv_d128.hip", "bwd.hip", "common.h"],
     "bwd_dq_kernel": ["bwd.hip", "common.h"],
 }
