@@ -84,6 +84,30 @@ def test_bwd_bitwise_deterministic(gpu_lib):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", [(1, 8, 2, 700, 700, 128, True), (2, 32, 8, 1000, 1000, 128, True),
+                                   (1, 4, 4, 300, 500, 64, False)])
+def test_bwd_stages_equal_whole(gpu_lib, shape):
+    """fa_bwd_stage 0 (dQ, with D and LSE*log2e into the workspace) then 1 (dK/dV) on one
+    stream gives exactly what fa_bwd gives, with workspaces that start out different."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, with_do=True, seed=3300 + Nq)
+    announce(f"bwd stages {shape}")
+    q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.fwd(q, k, v, causal=causal, scale=inp.scale)
+    nbytes = gpu_lib.bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+    ws_a = torch.zeros(nbytes, device=q.device, dtype=torch.uint8)
+    ws_b = torch.full((nbytes,), 0x7f, device=q.device, dtype=torch.uint8)
+    whole = gpu_lib.bwd(q, k, v, o, do, lse, causal=causal, scale=inp.scale, workspace=ws_a)
+    outs = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    for stage in (0, 1):
+        gpu_lib.bwd(q, k, v, o, do, lse, causal=causal, scale=inp.scale, dq=outs[0], dk=outs[1],
+                    dv=outs[2], workspace=ws_b, stage=stage)
+    torch.cuda.synchronize()
+    for x, y in zip(whole, outs):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 def test_c5_full_size_one_kv_group(gpu_lib):
     """The GQA training config at full size: the GPU computes every gradient; the
     oracle recomputes one (batch, kv-head) group in full (4 query heads, 8192 rows)."""
