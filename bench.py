@@ -305,8 +305,9 @@ def profile_tail(torch, fa, calls=3):
     """Counter-run mode only: short runs of the kernels outside the training step, so one
     rocprofv3 pass also covers them: fa_mfma_probe on normal-like bf16 operands (matrix
     cores busy by construction: the reference for the busy-cycle counter), the
-    non-causal B2 H16 N1024 d64 forward, and split-KV decode at B8 H8 Nk32768 d128 (one
-    row per kv-head) and B16 Hq32 Hkv4 Nk8192 d128 (eight rows)."""
+    non-causal B2 H16 N1024 d64 forward, split-KV decode at B8 H8 Nk32768 d128 (one row
+    per kv-head) and B16 Hq32 Hkv4 Nk8192 d128 (eight rows), and the causal forward at
+    B4 H32 N4096 d128, B2 H16 N4096 d256 and B1 H8 N32768 d128."""
     g = torch.Generator(device="cuda")
     g.manual_seed(99)
     out = torch.empty(1024 * 256, device="cuda", dtype=torch.float32)
@@ -322,6 +323,13 @@ def profile_tail(torch, fa, calls=3):
                          dtype=torch.uint8)
         for _ in range(calls):
             fa.fwd_splitkv(q, k, v, causal=True, workspace=ws)
+    # the causal forward workloads: B4 H32 N4096 d128, B2 H16 N4096 d256, B1 H8 N32768
+    # d128, two calls each (in this order)
+    for B, H, N, d in ((4, 32, 4096, 128), (2, 16, 4096, 256), (1, 8, 32768, 128)):
+        q, k, v = rnd(B, H, N, d), rnd(B, H, N, d), rnd(B, H, N, d)
+        for _ in range(2):
+            fa.fwd(q, k, v, causal=True)
+        del q, k, v
     torch.cuda.synchronize()
 
 
@@ -333,9 +341,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="counter-run mode: 1 GiB copy first, then the step; afterwards three "
-                         "calls each of the matrix-core probe, the d=64 forward and the two "
-                         "decode shapes; no oracle, no extras")
+                    help="counter-run mode: 1 GiB copy first, then the step; afterwards "
+                         "the matrix-core probe, the d=64 forward, the two decode shapes "
+                         "and the causal forward workloads; no oracle, no extras")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
