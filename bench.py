@@ -208,6 +208,7 @@ def extras(torch, fa, iters=20):
         out[name] = rec
         del q, k, v, o, lse
         torch.cuda.empty_cache()
+    out["c2_bf16_B2H16N1024d64_rotated"] = rotated_small(torch, fa, g)
     out["decode_gqa_B16Hq32Hkv4Nq1Nk8192d128"] = gqa_decode(torch, fa, g, iters)
     out["v1_vs_v2"] = version_ablation(torch, fa, g)
     out["fp8_forward"] = fp8_forward(torch, fa, g, out)
@@ -240,6 +241,35 @@ def fp8_forward(torch, fa, g, bf16_results, iters=20):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
     return res
+
+
+def rotated_small(torch, fa, g, sets=24, iters=96):
+    """The B2 H16 N1024 d64 forward with its inputs and outputs (16.9 MB per call)
+    rotated over `sets` copies, about 400 MB in all, more than the 256 MB last-level
+    cache: each call finds its operands in HBM, not in cache as when one set is timed
+    over and over."""
+    B, H, N, d = 2, 16, 1024, 64
+    bufs = []
+    for _ in range(sets):
+        q, k, v = (torch.randn(B, H, N, d, device="cuda", dtype=torch.bfloat16, generator=g)
+                   for _ in range(3))
+        bufs.append((q, k, v, torch.empty_like(q),
+                     torch.empty(B, H, N, device="cuda", dtype=torch.float32)))
+    turn = [0]
+
+    def call():
+        q, k, v, o, lse = bufs[turn[0] % sets]
+        turn[0] += 1
+        fa.fwd(q, k, v, causal=False, out=o, lse=lse)
+
+    ms = timed_ms(torch, call, iters)
+    fl = fwd_flops(B, H, N, N, d, False)
+    nbytes = 2 * 4 * B * H * N * d + 4 * B * H * N
+    del bufs
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+            "pct_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2),
+            "gbs": round(nbytes / ms / 1e6, 1), "input_sets": sets}
 
 
 def gqa_decode(torch, fa, g, iters):
