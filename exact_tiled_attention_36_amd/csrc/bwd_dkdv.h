@@ -1,6 +1,6 @@
 // The dK/dV kernel of the recompute backward and the parameter block the backward
-// kernels share, for gfx950. Included by bwd.hip (every head size but 128, and the
-// other backward kernels) and by bwd_dkdv_d128.hip (head size 128, built with a
+// kernels share, for gfx950. Included by bwd_dq.h (and so by bwd.hip, which launches
+// every head size but 128) and by bwd_dkdv_d128.hip (head size 128, built with a
 // compiler option of its own: see that file).
 #pragma once
 #include "common.h"

@@ -1,0 +1,258 @@
+// The dQ kernel of the recompute backward (the first of its two kernels), for gfx950.
+// Included by bwd.hip (8-wave workgroups, and d = 256) and by bwd_dq_small.hip (the
+// 4-wave d = 64 and d = 128 kernels for small grids, built with a compiler option of
+// their own: see that file).
+#pragma once
+#include "bwd_dkdv.h"
+
+namespace fa {
+
+// Launch of bwd_dq_kernel<d, 32, 4, causal> (d = 64 or 128) on `grid` workgroups
+// (bwd_dq_small.hip).
+hipError_t launch_bwd_dq_small(const BwdParams& p, int nqb, int grid, int d, bool causal,
+                               hipStream_t st);
+
+namespace {
+// ---------------------------------------------------------------------------------
+// 1. dQ, with D
+// ---------------------------------------------------------------------------------
+// One workgroup = NW waves x 32 query rows; Q and dO stay in registers, each wave
+// owns its rows' dQ. Key tiles of BN rows (K and V) are triple buffered in LDS and
+// copied two tiles ahead. Step t is one scheduling region:
+//   S, dP of tile t+1 (matrix)       with  dS of tile t (vector),
+//   dQ^T += K_t^T dS^T (matrix)      with  mask of tile t+1 (vector),
+// then the copies' wait and a barrier. S^T and dP^T put one query per lane, so LSE
+// and D are per-lane scalars; dS^T comes out in the B-operand layout of the dQ
+// product, and K^T is read with LDS transpose loads.
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
+  using TL = TileLayout<D>;
+  constexpr int TILE = TL::elems(BN);
+  constexpr int NDC = D / 16, NCB = D / 32, NKB = BN / 32;
+  constexpr int BM = 32 * NW;    // query rows per workgroup (one 32-row block per wave)
+  constexpr int NB = 3;
+  static_assert(TL::shifts_ok(BN), "LDS reads add row offsets as constants");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NB * 2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int qb, bh;
+  if (CAUSAL) {
+    causal_order<2>(blockIdx.x, gridDim.x, nqb, bh, qb);
+  } else {
+    qb = L % nqb;
+    bh = L / nqb;
+  }
+  const int h = bh % p.Hq, b = bh / p.Hq, kvh = h / p.g;
+  const int q0 = qb * BM;
+  const int w0 = q0 + 32 * wu;
+  const int qrow = w0 + l32;
+  const bool qvalid = qrow < p.Nq;
+  const size_t rowidx = (size_t)(b * p.Hq + h) * p.Nq + (qvalid ? qrow : p.Nq - 1);
+
+  bf16x8_t qreg[NDC], doreg[NDC];
+  {
+    const u32x4_t* qs = (const u32x4_t*)(p.q + rowidx * D + 8 * hi);
+    const u32x4_t* os = (const u32x4_t*)(p.dO + rowidx * D + 8 * hi);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      qreg[dc] = __builtin_bit_cast(bf16x8_t, qs[2 * dc]);
+      doreg[dc] = __builtin_bit_cast(bf16x8_t, os[2 * dc]);
+    }
+  }
+  // D_i = sum_c dO_ic O_ic: this lane's half of the row of O, read in the layout of
+  // dO, then the two halves combined. D and LSE * log2(e) also go to the workspace
+  // for the dK/dV kernel.
+  float dpart = 0.f;
+  {
+    const u32x4_t* os = (const u32x4_t*)(p.o + rowidx * D + 8 * hi);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      const u32x4_t ov = os[2 * dc];
+      const u32x4_t dv = __builtin_bit_cast(u32x4_t, doreg[dc]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dpart = fmaf(bf16_lo(ov[i]), bf16_lo(dv[i]), dpart);
+        dpart = fmaf(bf16_hi(ov[i]), bf16_hi(dv[i]), dpart);
+      }
+    }
+  }
+  const float dsum = xhalf_sum(dpart);
+  const float lraw = p.lse[rowidx];
+  const float Dv = qvalid ? dsum : 0.f;
+  const float lse2 = (!qvalid || lraw == -INFINITY) ? INFINITY : lraw * kLog2e;
+  if (qvalid && hi == 0) {
+    p.dvec[rowidx] = Dv;
+    p.lse2v[rowidx] = lse2;
+  }
+  // nothing may be outstanding in the loops below except the tile copies they issue
+  wait_vmem();
+
+  const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+  const uint16_t* Vg = p.v + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+  int kend = p.Nk;
+  if (CAUSAL) {
+    const int lim = q0 + BM + p.causal_off;
+    kend = lim < kend ? lim : kend;
+  }
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // tiles [0, tfull) are wholly visible to every row of the workgroup
+  int tfull = p.Nk / BN;
+  if (CAUSAL) {
+    const int lim = q0 + p.causal_off + 1;
+    tfull = min(tfull, lim > 0 ? lim / BN : 0);
+  }
+  tfull = min(tfull, ntiles);
+
+  f32x16_t dqacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dqacc[cb] = zero16();
+  const float c2 = p.scale_log2;
+
+  // buffer t%3 holds the K tile of key tile t, followed by its V tile
+  auto Kb = [&](int t) FA_INLINE { return smem + (t % NB) * 2 * TILE; };
+  // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
+  const uint32_t lane_off = 4u * lane;
+  auto load_tile = [&](int t) FA_INLINE {
+    if constexpr (D <= 128) {
+      if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
+        tile_load_full<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
+        tile_load_full<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
+        return;
+      }
+    }
+    tile_load_async<D, BN, NW>(Kg, t * BN, p.Nk, Kb(t), wu, lane);
+    tile_load_async<D, BN, NW>(Vg, t * BN, p.Nk, Kb(t) + TILE, wu, lane);
+  };
+
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint32_t srow = 2 * (TL::row(l32) + 8 * hi);
+  const uint32_t trow = 2 * (TL::row(tr_row) + tr_col);
+
+  // S^T = K Q^T and dP^T = V dO^T for key tile t
+  auto compute_sp = [&](f32x16_t (&S)[NKB], f32x16_t (&dP)[NKB], int t) FA_INLINE {
+    const uint32_t kbase = opaque(lds_addr(Kb(t)) + srow);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      S[kb] = zero16();
+      dP[kb] = zero16();
+    }
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t a = kbase + 2 * (TL::row(32 * kb) + 16 * dc);
+        S[kb] = mfma32x32x16(lds_read8_at(a), qreg[dc], S[kb]);
+        dP[kb] = mfma32x32x16(lds_read8_at(a + 2 * TILE), doreg[dc], dP[kb]);
+      }
+  };
+  // causal / key-tail mask of key tile t: masked scores give P = dS = 0
+  auto mask = [&](f32x16_t (&S)[NKB], int t) FA_INLINE {
+    const int j0 = t * BN;
+    const int lim = CAUSAL ? qrow + p.causal_off : 0x7fffffff;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (j >= p.Nk || j > lim) S[kb][r] = -INFINITY;
+      }
+  };
+  // dS = P * (dP - D) with P = exp2(S * scale * log2e - LSE2), bf16 pairs
+  auto dsoft = [&](f32x16_t (&S)[NKB], f32x16_t (&dP)[NKB], uint32_t (&dspk)[NKB][8]) FA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float pr = fast_exp2(fmaf(S[kb][r + e], c2, -lse2));
+          ds2[e] = pr * (dP[kb][r + e] - Dv);
+        }
+        dspk[kb][r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+      }
+  };
+  // dQ^T += K_t^T dS^T
+  auto dq_mm = [&](const uint32_t (&dspk)[NKB][8], int t) FA_INLINE {
+    const uint32_t tb = opaque(lds_addr(Kb(t)) + trow);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4_t du = {dspk[kb][4 * kk], dspk[kb][4 * kk + 1], dspk[kb][4 * kk + 2], dspk[kb][4 * kk + 3]};
+        const bf16x8_t db = __builtin_bit_cast(bf16x8_t, du);
+        const int R = 32 * kb + 16 * kk;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const bf16x8_t a = join8(lds_read_tr4_at(tb + 2 * (TL::row(R) + 32 * cb)),
+                                   lds_read_tr4_at(tb + 2 * (TL::row(R + 8) + 32 * cb)));
+          dqacc[cb] = mfma32x32x16(a, db, dqacc[cb]);
+        }
+      }
+  };
+
+  // Step t: entering, S/dP of tile t (masked) in (sc, pc), tiles t and t+1 in LDS.
+  // MASK: tile t+1 needs the mask; LAST: there is no tile t+1.
+  f32x16_t sA[NKB], pA[NKB], sB[NKB], pB[NKB];
+  uint32_t dspk[NKB][8];
+  auto step = [&](auto mask_tag, auto last_tag, f32x16_t (&sc)[NKB], f32x16_t (&pc)[NKB],
+                  f32x16_t (&sn)[NKB], f32x16_t (&pn)[NKB], int t) FA_INLINE {
+    constexpr bool MASK = decltype(mask_tag)::value, LAST = decltype(last_tag)::value;
+    if constexpr (!LAST) load_tile(t + 2);  // into the buffer of tile t-1, done with
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) compute_sp(sn, pn, t + 1);
+    dsoft(sc, pc, dspk);
+    dq_mm(dspk, t);
+    if constexpr (!LAST && MASK) mask(sn, t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) {
+      wait_vmem();
+      __syncthreads();
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    load_tile(1);
+    wait_vmem();
+    __syncthreads();
+    compute_sp(sA, pA, 0);
+    if (tfull == 0) mask(sA, 0);
+    int t = 0;
+    for (; t + 2 < tfull && t + 2 < ntiles; t += 2) {
+      step(BoolC<false>(), BoolC<false>(), sA, pA, sB, pB, t);
+      step(BoolC<false>(), BoolC<false>(), sB, pB, sA, pA, t + 1);
+    }
+    for (; t + 2 < ntiles; t += 2) {
+      step(BoolC<true>(), BoolC<false>(), sA, pA, sB, pB, t);
+      step(BoolC<true>(), BoolC<false>(), sB, pB, sA, pA, t + 1);
+    }
+    if (t + 1 < ntiles) {
+      step(BoolC<true>(), BoolC<false>(), sA, pA, sB, pB, t);
+      step(BoolC<false>(), BoolC<true>(), sB, pB, sA, pA, t + 1);
+    } else {
+      step(BoolC<false>(), BoolC<true>(), sA, pA, sB, pB, t);
+    }
+  }
+
+  if (qvalid) {
+    uint16_t* orow = p.dq + rowidx * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = 32 * cb + 8 * rg + 4 * hi;
+        const u32x2_t val = {pack_bf16x2(dqacc[cb][4 * rg] * p.scale, dqacc[cb][4 * rg + 1] * p.scale),
+                             pack_bf16x2(dqacc[cb][4 * rg + 2] * p.scale, dqacc[cb][4 * rg + 3] * p.scale)};
+        *(u32x2_t*)(orow + c0) = val;
+      }
+  }
+}
+
+}  // namespace
+}  // namespace fa

@@ -1,0 +1,29 @@
+// dQ kernels for small grids (4 waves, d = 64 and 128) in a translation unit of their
+// own. build.py compiles this file with -mllvm --amdgpu-mfma-vgpr-form: the matrix
+// products write ordinary vector registers, so the softmax reads S and dP without a
+// v_accvgpr_read per element (a step of these kernels issues 193 vector instructions
+// instead of 257). The option is kept off the other dQ builds: it leaves the 8-wave
+// kernels unchanged and makes the d = 256 one spill.
+#include "bwd_dq.h"
+
+namespace fa {
+
+hipError_t launch_bwd_dq_small(const BwdParams& p, int nqb, int grid, int d, bool causal,
+                               hipStream_t st) {
+  if (d == 64) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<64, 32, 4, true>), dim3(grid), dim3(256), 0, st, p, nqb);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<64, 32, 4, false>), dim3(grid), dim3(256), 0, st, p, nqb);
+  } else if (d == 128) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<128, 32, 4, true>), dim3(grid), dim3(256), 0, st, p, nqb);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<128, 32, 4, false>), dim3(grid), dim3(256), 0, st, p, nqb);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa
