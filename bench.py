@@ -54,7 +54,11 @@ def fwd_flops(B, Hq, Nq, Nk, d, causal):
 
 
 def source_sha(kernel):
+    """Hash of the kernel's sources and of the build script (its per-file compiler
+    options change the binary too)."""
     h = hashlib.sha256()
+    with open(os.path.join(ROOT, "exact_tiled_attention_36_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "exact_tiled_attention_36_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
