@@ -27,10 +27,12 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 # Options for single files: the d = 128 dK/dV kernel and the small-grid forward and dQ kernels
-# have their matrix products write ordinary vector registers (see the files' headers); the
-# other backward kernels are scheduled by the compiler's iterative-ILP strategy (the 8-wave
-# dQ kernel 1-4 % faster than with the default scheduler, no kernel in that file spills more).
-FILE_FLAGS = {"bwd_dkdv_d128.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+# have their matrix products write ordinary vector registers (see the files' headers). The
+# d = 128 dK/dV kernel is scheduled by the compiler's max-ILP strategy (0.6-2 % faster than
+# the default, no scratch), the other backward kernels by its iterative-ILP strategy (the
+# 8-wave dQ kernel 1-4 % faster, no kernel in that file spills more).
+FILE_FLAGS = {"bwd_dkdv_d128.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form",
+                                    "-mllvm", "--amdgpu-sched-strategy=max-ilp"],
               "fwd_bf16_small.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
               "bwd_dq_small.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
               "bwd.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-ilp"]}
