@@ -18,10 +18,10 @@ size is one of the pins of the oracle.
   unnormalised, is rescaled only by exp(m_old - m_new) per block, and is divided by
   l once after the last block. Q is tiled in an outer loop and K/V in an inner loop,
   as in §三 (the complete computation graph).
-* ``kv_blocked_all_rows``: the FlashAttention1 article's pseudo-implementation
-  (gitcode.csdn.net, §三): every query row at once, K/V blocks in a loop, running
-  max and normaliser, one division after the loop; the last block is clipped to
-  the sequence length.
+
+The FlashAttention1 article (gitcode.csdn.net, §三) describes the same deferred
+recurrence with every query row in one block and K/V blocks clipped to the sequence
+length; ``online_v2`` with ``block_q`` = the number of query rows is that case.
 """
 from __future__ import annotations
 
@@ -89,22 +89,3 @@ def online_v2(q, k, v, scale, block_q, block_k, causal=False):
             lse[rows] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return o, lse
 
-
-def kv_blocked_all_rows(q, k, v, block_size, scale=None):
-    """Batched [batch, seq, d] form; scale defaults to 1/sqrt(d_k) as on the page."""
-    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
-    bs, nq, dk = q.shape
-    nk = k.shape[1]
-    sc = 1.0 / np.sqrt(dk) if scale is None else scale
-    out = np.zeros((bs, nq, v.shape[2]))
-    l = np.zeros((bs, nq, 1))
-    m = np.full((bs, nq, 1), -np.inf)
-    for start in range(0, nk, block_size):
-        end = min(start + block_size, nk)
-        s = (q @ np.swapaxes(k[:, start:end], 1, 2)) * sc
-        m_new = np.maximum(m, s.max(axis=-1, keepdims=True))
-        e = np.exp(s - m_new)
-        l_new = l * np.exp(m - m_new) + e.sum(axis=-1, keepdims=True)
-        out = out * np.exp(m - m_new) + e @ v[:, start:end]
-        m, l = m_new, l_new
-    return out / l

@@ -147,12 +147,11 @@ def pin_recurrences(fwd):
                 o2, l2 = online.online_v2(q, k, v, sc, bq, bk, causal)
                 np.testing.assert_allclose(o2, o_ref, atol=1e-12, rtol=0)
                 np.testing.assert_allclose(l2, l_ref, atol=1e-12, rtol=0)
-    # the batched K/V-block form of the FlashAttention1 article, scale 1/sqrt(d_k)
-    qb, kb, vb = q[None].repeat(2, 0), k[None].repeat(2, 0), v[None].repeat(2, 0)
-    o_ref = fwd(qb[:, None], kb[:, None], vb[:, None], 1 / math.sqrt(d), False)[0][:, 0]
+    # the FlashAttention1 article's case: all query rows in one block, scale 1/sqrt(d_k)
+    o_ref = fwd(q[None, None], k[None, None], v[None, None], 1 / math.sqrt(d), False)[0][0, 0]
     for bs in range(1, N + 1):
-        np.testing.assert_allclose(online.kv_blocked_all_rows(qb, kb, vb, bs), o_ref,
-                                   atol=1e-12, rtol=0)
+        o_pg, _ = online.online_v2(q, k, v, 1 / math.sqrt(d), N, bs)
+        np.testing.assert_allclose(o_pg, o_ref, atol=1e-12, rtol=0)
 
 
 def pin_torch_sdpa(fwd, bwd):
@@ -335,8 +334,9 @@ def test_pages_printed_figures():
     assert (c2["B"], c2["Nq"], c2["d"]) == (h["batch"], h["seq_len"], h["d"])
     # the harness's block size of 256 gives the same result as the direct form
     q, k, v, _ = problem(1, 1, 1, 300, 300, 8, 80)
-    o_ref = A.forward(q, k, v, 1 / math.sqrt(8), False)[0][0]
-    o_pg = online.kv_blocked_all_rows(q[0], k[0], v[0], h["block_size"])
+    o_ref = A.forward(q, k, v, 1 / math.sqrt(8), False)[0][0, 0]
+    o_pg, _ = online.online_v2(q[0, 0], k[0, 0], v[0, 0], 1 / math.sqrt(8), 300,
+                               h["block_size"])
     np.testing.assert_allclose(o_pg, o_ref, atol=1e-12)
 
 
