@@ -13,8 +13,12 @@ Prints one JSON line. Besides the headline value it carries:
                 the matrix-core rate measured on this GPU (fa_mfma_probe, zeros and
                 normal-like bf16 operands) with the kernel's fraction of the latter;
   cpu_baseline  the float64 oracle on this host, timed on a bounded sample;
-  phases        per-kernel average milliseconds;
-  extra         forward/decode throughput of the other workloads (fewer iterations).
+  phases        per-kernel average milliseconds over the timed steps;
+  median_ms, min_ms, step_stats
+                the step and each kernel timed one by one over --stat-steps (50)
+                further steps: mean, median and minimum;
+  extra         forward/decode throughput of the other workloads (50 calls each, an
+                event pair per call: mean, median, minimum).
 
 Modes: default; --profile (no oracle/extras, a known-size copy first, for rocprofv3
 counter runs that calibrate FETCH_SIZE/WRITE_SIZE; after the step, short runs of the
@@ -103,6 +107,9 @@ class Timer:
     def avg_ms(self):
         return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.pairs.items()}
 
+    def stats(self):
+        return {k: summarize([a.elapsed_time(b) for a, b in v]) for k, v in self.pairs.items()}
+
 
 def cpu_baseline(inp, min_seconds=10.0):
     """The float64 oracle, as written, on a bounded sample of the workload: whole
@@ -137,26 +144,72 @@ def cpu_baseline(inp, min_seconds=10.0):
                       "S and P materialised"}
 
 
-def timed_ms(torch, call, iters, warm_ms=50.0):
-    """Average milliseconds per call over iters calls on the current stream, after
-    warm-up calls until at least warm_ms of GPU time has passed (at least three), so
-    that short kernels are timed at the clock a sustained run reaches."""
+def warm(torch, call, warm_ms=50.0, min_calls=10):
+    """Warm-up calls until at least warm_ms of GPU time has passed and at least
+    min_calls calls were made, so that short kernels are timed at the clock a sustained
+    run reaches."""
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     spent, n = 0.0, 0
-    while n < 3 or spent < warm_ms:
+    while n < min_calls or spent < warm_ms:
         e0.record(st)
         call()
         e1.record(st)
         torch.cuda.synchronize()
         spent += e0.elapsed_time(e1)
         n += 1
+
+
+def summarize(times):
+    """mean, median and min of a list of milliseconds."""
+    import statistics
+    return {"mean_ms": round(sum(times) / len(times), 4),
+            "median_ms": round(statistics.median(times), 4),
+            "min_ms": round(min(times), 4), "calls": len(times)}
+
+
+def timed_stats(torch, call, iters=50, warm_ms=50.0):
+    """Per-call milliseconds of iters calls issued back to back on the current stream
+    (one pair of HIP events around each call), after warm-up; returns mean, median and
+    min."""
+    warm(torch, call, warm_ms)
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record(st)
+        call()
+        b.record(st)
+    torch.cuda.synchronize()
+    return summarize([a.elapsed_time(b) for a, b in ev])
+
+
+def timed_ms(torch, call, iters, warm_ms=50.0):
+    """Average milliseconds per call over iters back-to-back calls on the current
+    stream (one event pair around all of them), after warm-up."""
+    warm(torch, call, warm_ms, min_calls=3)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(iters):
         call()
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters
+
+
+def with_stats(rec, st, flops=None):
+    """Fold timed_stats() output into a result record: ms is the mean; median and min
+    are kept beside it (TFLOP/s from the mean)."""
+    rec["ms"] = st["mean_ms"]
+    rec["median_ms"] = st["median_ms"]
+    rec["min_ms"] = st["min_ms"]
+    rec["calls"] = st["calls"]
+    if flops is not None:
+        rec["tflops"] = round(flops / st["mean_ms"] / 1e9, 1)
+        rec["tflops_at_median"] = round(flops / st["median_ms"] / 1e9, 1)
+        rec["pct_bf16_peak"] = round(flops / st["mean_ms"] / 1e9 / PEAK_BF16_TFLOPS * 100, 2)
+    return rec
 
 
 def mfma_ceiling(torch, fa, blocks=4096, iters=400, reps=5):
@@ -177,8 +230,9 @@ def mfma_ceiling(torch, fa, blocks=4096, iters=400, reps=5):
     return res
 
 
-def extras(torch, fa, iters=20):
-    """Forward throughput on the other workloads, decode in GB/s (seeded torch.randn)."""
+def extras(torch, fa, iters=50):
+    """Forward throughput on the other workloads, decode in GB/s (seeded torch.randn);
+    each timing is iters calls with an event pair per call (mean, median, min)."""
     from exact_tiled_attention_36_amd import synth
     out = {}
     g = torch.Generator(device="cuda")
@@ -200,10 +254,9 @@ def extras(torch, fa, iters=20):
             call = lambda: fa.fwd_splitkv(q, k, v, causal=causal, out=o, lse=lse, workspace=ws)
         else:
             call = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-        ms = timed_ms(torch, call, iters)
         fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
-        rec = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
-               "pct_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2)}
+        rec = with_stats({}, timed_stats(torch, call, iters), fl)
+        ms = rec["ms"]
         if decode:
             nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
             rec["gbs"] = round(nbytes / ms / 1e6, 1)
@@ -219,7 +272,7 @@ def extras(torch, fa, iters=20):
     return out
 
 
-def fp8_forward(torch, fa, g, bf16_results, iters=20):
+def fp8_forward(torch, fa, g, bf16_results, iters=50):
     """fa_fwd_fp8 on the shapes of the d=128 causal bf16 forward workloads: E4M3 inputs
     from seeded torch.randn scaled by 32 (per-tensor descale 1/32), FLOPs counted as for
     bf16, against the dense FP8 MFMA peak, with the speedup over fa_fwd on the same
@@ -234,11 +287,12 @@ def fp8_forward(torch, fa, g, bf16_results, iters=20):
         o = torch.empty(B, Hq, Nq, d, device="cuda", dtype=torch.bfloat16)
         lse = torch.empty(B, Hq, Nq, device="cuda", dtype=torch.float32)
         call = lambda: fa.fwd_fp8(q, k, v, 1 / 32, 1 / 32, 1 / 32, causal=causal, out=o, lse=lse)
-        ms = timed_ms(torch, call, iters)
         fl = fwd_flops(B, Hq, Nq, Nk, d, causal)
-        rec = {"workload": name.replace("bf16", "fp8"), "ms": round(ms, 4),
-               "tflops": round(fl / ms / 1e9, 1),
-               "pct_fp8_peak": round(fl / ms / 1e9 / PEAK_FP8_TFLOPS * 100, 2)}
+        rec = with_stats({"workload": name.replace("bf16", "fp8")},
+                         timed_stats(torch, call, iters), fl)
+        del rec["pct_bf16_peak"]
+        ms = rec["ms"]
+        rec["pct_fp8_peak"] = round(fl / ms / 1e9 / PEAK_FP8_TFLOPS * 100, 2)
         if name in bf16_results:
             rec["speedup_over_bf16_fwd"] = round(bf16_results[name]["ms"] / ms, 3)
         res[name.replace("bf16", "fp8")] = rec
@@ -266,14 +320,13 @@ def rotated_small(torch, fa, g, sets=24, iters=96):
         turn[0] += 1
         fa.fwd(q, k, v, causal=False, out=o, lse=lse)
 
-    ms = timed_ms(torch, call, iters)
     fl = fwd_flops(B, H, N, N, d, False)
+    rec = with_stats({}, timed_stats(torch, call, iters), fl)
     nbytes = 2 * 4 * B * H * N * d + 4 * B * H * N
     del bufs
     torch.cuda.empty_cache()
-    return {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
-            "pct_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2),
-            "gbs": round(nbytes / ms / 1e6, 1), "input_sets": sets}
+    rec.update({"gbs": round(nbytes / rec["ms"] / 1e6, 1), "input_sets": sets})
+    return rec
 
 
 def gqa_decode(torch, fa, g, iters):
@@ -288,13 +341,15 @@ def gqa_decode(torch, fa, g, iters):
     ws = torch.empty(fa.splitkv_workspace_bytes(B, Hq, Hkv, 1, Nk, d), device="cuda",
                      dtype=torch.uint8)
     call = lambda: fa.fwd_splitkv(q, k, v, causal=True, out=o, lse=lse, workspace=ws)
-    ms = timed_ms(torch, call, iters)
+    rec = with_stats({}, timed_stats(torch, call, iters))
+    ms = rec["ms"]
     nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
-    return {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
-            "pct_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS * 100, 2),
-            "kernel": "fa_fwd_splitkv (matrix-core chunks + merge)"}
+    rec.update({"gbs": round(nbytes / ms / 1e6, 1),
+                "pct_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS * 100, 2),
+                "kernel": "fa_fwd_splitkv (matrix-core chunks + merge)"})
+    return rec
 
 
 def version_ablation(torch, fa, g, iters=5, reps=5):
@@ -372,6 +427,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--stat-steps", type=int, default=50,
+                    help="steps timed one by one after the timed region (median, min)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--profile", action="store_true",
@@ -418,14 +475,17 @@ def main():
 
     timer = Timer(torch, stream)
 
-    def step(record):
-        run = timer.mark if record else (lambda name, fn: fn())
+    def step_marks(tm):
+        run = tm.mark if tm is not None else (lambda name, fn: fn())
         run("fwd_bf16_kernel", lambda: fa.fwd(q, k, v, causal=causal, scale=inp.scale,
                                               out=o, lse=lse))
         for stg, name in ((0, "bwd_dq_kernel"), (1, "bwd_dkdv_kernel")):
             run(name, lambda stg=stg: fa.bwd(q, k, v, o, do, lse, causal=causal,
                                              scale=inp.scale, dq=dq, dk=dk, dv=dv,
                                              workspace=ws, stage=stg))
+
+    def step(record):
+        step_marks(timer if record else None)
 
     for _ in range(args.warmup):
         step(False)
@@ -441,6 +501,21 @@ def main():
     f_step = 3.5 * f_fwd
     value = args.steps * f_step / elapsed / 1e12
     ms = timer.avg_ms()
+
+    # Statistics pass after the timed region: STAT_STEPS more steps, each bracketed by
+    # its own event pair (and each kernel by one), for the median and minimum.
+    step_stats, phase_stats = {"median_ms": None, "min_ms": None}, {}
+    if args.stat_steps > 0 and not args.profile:
+        log(f"statistics over {args.stat_steps} steps")
+        stat_timer = Timer(torch, stream)
+        for _ in range(args.stat_steps):
+            stat_timer.mark("step", lambda: step(False))
+        inner = Timer(torch, stream)
+        for _ in range(args.stat_steps):
+            step_marks(inner)
+        torch.cuda.synchronize()
+        step_stats = stat_timer.stats()["step"]
+        phase_stats = inner.stats()
 
     # algorithmic flops per launch: dense products each kernel performs (causal halved)
     per_kernel_flops = {"fwd_bf16_kernel": f_fwd, "bwd_dkdv_kernel": 2 * f_fwd,
@@ -464,6 +539,10 @@ def main():
         "pct_bf16_peak": round(value / PEAK_BF16_TFLOPS * 100, 2),
         "roofline": roofline,
         "phases_ms": {kname: round(t, 4) for kname, t in ms.items()},
+        "median_ms": step_stats["median_ms"], "min_ms": step_stats["min_ms"],
+        "step_stats": {"step": step_stats, **phase_stats,
+                       "note": f"{args.stat_steps} further steps after the timed region, "
+                               "one event pair per step (and, in a second pass, per kernel)"},
         "phase_tflops": {"fwd": round(f_fwd / ms["fwd_bf16_kernel"] / 1e9, 1),
                          "bwd": round(2.5 * f_fwd / (ms["bwd_dkdv_kernel"] + ms["bwd_dq_kernel"])
                                      / 1e9, 1)},

@@ -201,10 +201,11 @@ __device__ __forceinline__ void lds_dma_dword(const void* src, const void* lds_b
 
 // Same copy with a wave-uniform global base and a per-lane byte offset (the saddr
 // form): lane i reads gbase + lane_off. With lane_off = 4*lane a wave copies 256
-// contiguous bytes at no vector-ALU cost. No memory clobber: the caller guarantees
-// that nothing reads the destination before its wait_vmem() and barrier, and that no
-// wave still reads it when the copy is issued; volatile asm keeps its order relative
-// to those barriers.
+// contiguous bytes at no vector-ALU cost. The caller guarantees that nothing reads the
+// destination before its wait_vmem() and barrier, and that no wave still reads it when
+// the copy is issued; the memory clobber keeps every other memory access of the wave on
+// its side of the copy as well, so that order never rests on how the compiler treats
+// volatile asm next to ordinary loads and stores.
 __device__ __forceinline__ void lds_dma_row(const void* gbase, uint32_t lane_off,
                                             const void* lds_base) {
   const uint32_t m0v = (uint32_t)(uintptr_t)(const FA_LDS void*)lds_base;
@@ -214,7 +215,7 @@ __device__ __forceinline__ void lds_dma_row(const void* gbase, uint32_t lane_off
       "global_load_lds_dword %0, %1"
       :
       : "v"(lane_off), "s"(gbase), "s"(m0v)
-      : "m0");
+      : "memory", "m0");
 }
 
 // Same copy with a scalar base, a per-lane byte offset and an immediate offset IMM
@@ -230,7 +231,7 @@ __device__ __forceinline__ void lds_dma_row_imm(const void* gbase, uint32_t lane
       "global_load_lds_dword %0, %1 offset:%3"
       :
       : "v"(lane_off), "s"(gbase), "s"(lds_m0), "i"(IMM)
-      : "m0");
+      : "memory", "m0");
 }
 
 // Four copies of the saddr form that share one M0 write: copy c reads
@@ -250,7 +251,7 @@ __device__ __forceinline__ void lds_dma_row_x4(const void* gbase, uint32_t v0, u
       :
       : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(gbase), "s"(lds_m0), "i"(I0), "i"(I1), "i"(I2),
         "i"(I3)
-      : "m0");
+      : "memory", "m0");
 }
 
 // Asynchronous copy of a [ROWS][D] bf16 tile (global rows j0.. of G, clamped to

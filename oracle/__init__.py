@@ -9,7 +9,7 @@ and torch's CPU float64 attention).
 
 Modules:
   attention  exact forward/backward from the definition (numpy float64)
-  online     the pages' block recurrences (v1 normalised, v2 deferred, pg2 batched)
+  online     the pages' block recurrences (v1 normalised, v2 deferred)
   scalar     brute force with Python floats, math.fsum and math.exp
   fp8        E4M3 decoding, the FP8 forward's reference and its weight-rounding bound
 """

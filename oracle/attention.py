@@ -119,6 +119,18 @@ def forward_rows(q, k, v, scale: float, causal: bool, b: int, h: int,
     return o, lse
 
 
+def forward_head(q, k, v, scale: float, causal: bool, b: int, h: int):
+    """O [Nq,d] and LSE [Nq] of one head (b, h), every row."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Nq = q.shape[2]
+    o = np.zeros((Nq, v.shape[3]))
+    lse = np.zeros(Nq)
+    for r0 in range(0, Nq, _ROW_BLOCK):
+        rows = np.arange(r0, min(Nq, r0 + _ROW_BLOCK))
+        o[rows], lse[rows] = forward_rows(q, k, v, scale, causal, b, h, rows)
+    return o, lse
+
+
 def forward(q, k, v, scale: float, causal: bool):
     """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] in float64."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -127,10 +139,7 @@ def forward(q, k, v, scale: float, causal: bool):
     lse = np.zeros((B, Hq, Nq))
     for b in range(B):
         for h in range(Hq):
-            for r0 in range(0, Nq, _ROW_BLOCK):
-                rows = np.arange(r0, min(Nq, r0 + _ROW_BLOCK))
-                o[b, h, rows], lse[b, h, rows] = forward_rows(
-                    q, k, v, scale, causal, b, h, rows)
+            o[b, h], lse[b, h] = forward_head(q, k, v, scale, causal, b, h)
     return o, lse
 
 

@@ -43,6 +43,30 @@ SHAPES = [
     (1, 2, 2, 130, 260, 256, False),
 ]
 
+# Head size 256 (the d = 256 dQ and dK/dV kernels): GQA and MQA groups, N >= 1000,
+# causal with ragged tails on both sides, both causal alignments, large logits.
+SHAPES_D256 = [
+    (1, 8, 2, 1000, 1000, 256, True),
+    (2, 4, 1, 1030, 1030, 256, True),
+    (1, 4, 2, 1100, 700, 256, False),
+    (1, 2, 1, 700, 1300, 256, True),
+    (1, 6, 3, 1027, 1027, 256, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_D256)
+def test_bwd_d256(gpu_lib, shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, with_do=True,
+                            seed=3400 + Nq + 3 * Nk + Hq)
+    check(gpu_lib, inp, f"bwd-d256{shape}")
+
+
+def test_bwd_d256_large_logits(gpu_lib):
+    inp = synth.make_inputs(1, 4, 2, 1000, 1000, 256, causal=True, with_do=True, seed=3450,
+                            q_mult=4.0)
+    check(gpu_lib, inp, "bwd d256 q*4")
+
 
 @pytest.mark.parametrize("shape", SHAPES)
 def test_bwd_shapes(gpu_lib, shape):
@@ -75,9 +99,10 @@ def test_bwd_large_logits(gpu_lib):
     check(gpu_lib, inp, "bwd q*4")
 
 
-def test_bwd_bitwise_deterministic(gpu_lib):
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_bitwise_deterministic(gpu_lib, d):
     import torch
-    inp = synth.make_inputs(1, 8, 2, 700, 700, 128, causal=True, with_do=True, seed=3200)
+    inp = synth.make_inputs(1, 8, 2, 700, 700, d, causal=True, with_do=True, seed=3200)
     a = gpu_fwd_bwd(gpu_lib, inp)
     b = gpu_fwd_bwd(gpu_lib, inp)
     for x, y in zip(a, b):

@@ -155,26 +155,48 @@ def test_no_quadratic_buffer(gpu_lib):
     assert extra < 4096 * 4096 * 2
 
 
-SAMPLED = ["c3a_bf16_causal_B4H32N4096d128", "c3b_bf16_causal_B2H16N4096d256",
-           "c4a_bf16_causal_B1H8N32768d128", "c5_bf16_causal_gqa_B2Hq32Hkv8N8192d128"]
+# Full-size configurations: whole heads compared row by row, plus sampled rows of
+# random heads. Workgroup id hw runs on XCD hw % 8, and with (batch x head) a multiple
+# of 8 the causal order gives XCD x the heads x*k .. x*k+k-1 (k = B*Hq/8), in pairs
+# when k > 1 and alone when k = 1 (the B1 H8 workload). The first and the last
+# (batch, head) therefore sit on the first and the last XCD; a middle one is added
+# where a head costs the oracle little.
+FULL = {
+    "c3a_bf16_causal_B4H32N4096d128": [(0, 0), (2, 5), (3, 31)],
+    "c3b_bf16_causal_B2H16N4096d256": [(0, 0), (1, 2), (1, 15)],
+    "c4a_bf16_causal_B1H8N32768d128": [(0, 0), (0, 7)],
+    "c5_bf16_causal_gqa_B2Hq32Hkv8N8192d128": [(0, 0), (1, 13), (1, 31)],
+}
 
 
-@pytest.mark.parametrize("name", SAMPLED)
-def test_full_size_sampled_rows(gpu_lib, name):
-    """Full-size configs: every output is computed on the GPU; sampled (b, h, rows)
-    are recomputed by the oracle one by one."""
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_whole_heads(gpu_lib, name):
+    """Every output is computed on the GPU and checked finite; the listed (b, h) are
+    compared with the oracle on every row (max and mean of |O - O_ref| over those
+    heads, and LSE), and sampled rows of random heads one by one."""
     import torch
     inp = synth.workload(name, with_do=False)
     announce(f"full-size fwd {name}")
     o, lse = run_fwd(gpu_lib, inp)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    rng = np.random.default_rng(5)
     qf, kf, vf = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for b, h in FULL[name]:
+        o_ref, lse_ref = A.forward_head(qf, kf, vf, inp.scale, inp.causal, b, h)
+        assert_o_close(o[b, h], o_ref, f"{name} whole head b{b} h{h}")
+        assert_lse_close(lse[b, h], lse_ref, TOL_LSE_BF16, f"{name} whole head b{b} h{h}")
+        got_o.append(o[b, h]), ref_o.append(o_ref), got_l.append(lse[b, h])
+        ref_l.append(lse_ref)
+    mx, mean = assert_o_close(np.stack(got_o), np.stack(ref_o), f"{name} whole heads")
+    lmx = assert_lse_close(np.stack(got_l), np.stack(ref_l), TOL_LSE_BF16, name)
+    print(f"[gpu-case] {name}: {len(got_o)} whole heads, O max {mx:.3e} mean {mean:.3e}, "
+          f"LSE max {lmx:.3e}", flush=True)
+    rng = np.random.default_rng(5)
     for _ in range(3):
         b, h = int(rng.integers(inp.B)), int(rng.integers(inp.Hq))
         rows = np.unique(np.concatenate([[0, inp.Nq - 1], rng.integers(0, inp.Nq, 20)]))
         o_ref, lse_ref = A.forward_rows(qf, kf, vf, inp.scale, inp.causal, b, h, rows)
         assert_o_close(o[b, h, rows], o_ref, f"{name} b{b} h{h}")
         assert_lse_close(lse[b, h, rows], lse_ref, TOL_LSE_BF16, f"{name} b{b} h{h}")
-    del inp
+    del inp, qf, kf, vf
     torch.cuda.empty_cache()
