@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "kernels.h"
 
@@ -47,6 +49,31 @@ size_t splitkv_part_lse_bytes(int B, int Hq, int Nq, int splits) {
   return align256((size_t)B * Hq * Nq * splits * sizeof(float));
 }
 
+// Device-resident scratch of fa_bwd_noalloc: D_i and the log2-scaled lse of up to
+// FA_BWD_NOALLOC_MAX_ROWS query rows (the workspace fa_bwd takes from its caller).
+// Every GPU the library runs on holds its own copy until the process ends.
+static __device__ __align__(256) float scratch[2 * (size_t)FA_BWD_NOALLOC_MAX_ROWS];
+
+// Device address of `scratch` on each device, looked up once per device with that
+// device current. In host code the array's name is only a host-side stand-in; every
+// kernel argument uses the address kept here.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+    scratch_ptr[dev] = (float*)p;
+  }
+  *out = scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,6 +95,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale (and every FP8 descale) must be finite and > 0";
     case FA_ERR_STAGE: return "FA_ERR_STAGE: backward stage must be 0 or 1";
     case FA_ERR_VARIANT: return "FA_ERR_VARIANT: forward variant must be 0, 1, 2 or 3";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: B * Hq * Nq exceeds FA_BWD_NOALLOC_MAX_ROWS (fa_bwd_noalloc's "
+             "fixed scratch); use fa_bwd with a workspace";
     default: return "unknown fa status code";
   }
 }
@@ -165,11 +195,9 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   return align256(2 * (size_t)B * Hq * Nq * sizeof(float));
 }
 
-static int bwd_common(const void* q, const void* k, const void* v, const void* o,
-                      const void* dO, const float* lse, void* dq, void* dk, void* dv,
-                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                      int Nq, int Nk, int d, float scale, int causal, int stage,
-                      void* stream) {
+static int bwd_check(const void* q, const void* k, const void* v, const void* o,
+                     const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, float scale) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d, scale);
   if (st != FA_OK) return st;
@@ -177,6 +205,16 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+static int bwd_common(const void* q, const void* k, const void* v, const void* o,
+                      const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, float scale, int causal, int stage,
+                      void* stream) {
+  int st = bwd_check(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
   if (!workspace || !aligned16(workspace) ||
       workspace_bytes < fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
     return FA_ERR_WORKSPACE;
@@ -192,6 +230,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int causal, void* stream) {
   return bwd_common(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
                     Nq, Nk, d, scale, causal, -1, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   void* stream) {
+  int st = bwd_check(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK) return st;
+  if ((long long)B * Hq * Nq > FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+  float* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != FA_OK) return st;
+  // Nothing in the scratch needs clearing: the dQ kernel writes D and the scaled lse of
+  // every row before the dK/dV kernel, queued after it on the same stream, reads them.
+  return launch_status(fa::launch_bwd(
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+      (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, ws,
+      shape(B, Hq, Hkv, Nq, Nk, d, scale, causal), -1, (hipStream_t)stream));
 }
 
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,

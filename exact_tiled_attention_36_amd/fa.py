@@ -38,6 +38,7 @@ _SIGNATURES = {
     "fa_bwd": (_c_int, [_vp] * 10 + [_c_size] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
     "fa_bwd_stage": (_c_int, [_c_int] + [_vp] * 10 + [_c_size] + [_c_int] * 6
                      + [_c_float, _c_int, _vp]),
+    "fa_bwd_noalloc": (_c_int, [_vp] * 9 + [_c_int] * 6 + [_c_float, _c_int, _vp]),
     "fa_fwd_variant_workspace_bytes": (_c_size, [_c_int] * 7),
     "fa_fwd_variant": (_c_int, [_vp] * 6 + [_c_size] + [_c_int] * 6
                        + [_c_float, _c_int, _c_int, _vp]),
@@ -279,6 +280,30 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
         _launch("fa_bwd", lib.fa_bwd, q.device, *args)
     else:
         _launch("fa_bwd_stage", lib.fa_bwd_stage, q.device, int(stage), *args)
+    return dq, dk, dv
+
+
+# Largest B * Hq * Nq that fa_bwd_noalloc takes (include/fa.h).
+BWD_NOALLOC_MAX_ROWS = 1048576
+
+
+def bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False,
+                scale: Optional[float] = None):
+    """dQ, dK, dV (bf16) through fa_bwd_noalloc: the library's own fixed scratch instead
+    of a workspace. The output buffers are required (nothing is allocated here either)."""
+    import torch
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = _inp(o, q.shape, q.dtype, q.device, "o")
+    do = _inp(do, q.shape, q.dtype, q.device, "do")
+    lse = _inp(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
+    dq = _inp(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _inp(dk, k.shape, k.dtype, k.device, "dk")
+    dv = _inp(dv, v.shape, v.dtype, v.device, "dv")
+    _launch("fa_bwd_noalloc", lib.fa_bwd_noalloc, q.device, q.data_ptr(), k.data_ptr(),
+            v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)))
     return dq, dk, dv
 
 

@@ -60,8 +60,12 @@ enum {
   FA_ERR_SPLITS = -9,     /* num_splits out of range                             */
   FA_ERR_SCALE = -10,     /* scale (or an FP8 descale) is not a finite number > 0 */
   FA_ERR_STAGE = -11,     /* fa_bwd_stage: stage not in {0, 1}                   */
-  FA_ERR_VARIANT = -12    /* fa_fwd_variant: variant not in {0, 1, 2, 3}         */
+  FA_ERR_VARIANT = -12,   /* fa_fwd_variant: variant not in {0, 1, 2, 3}         */
+  FA_ERR_SCRATCH = -13    /* fa_bwd_noalloc: B * Hq * Nq > FA_BWD_NOALLOC_MAX_ROWS */
 };
+
+/* Largest B * Hq * Nq that fa_bwd_noalloc accepts (its scratch: 8 MiB per GPU). */
+#define FA_BWD_NOALLOC_MAX_ROWS 1048576
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int fa_version(void);
@@ -148,6 +152,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
            float scale, int causal, void* stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, results and errors as fa_bwd minus the workspace; the
+ * call allocates nothing (no hipMalloc, hipFree or allocating library routine). D_i
+ * and the log2-scaled lse live in a fixed device array of the library instead, 8 MiB
+ * on every GPU it runs on, held until the process ends: B * Hq * Nq must not exceed
+ * FA_BWD_NOALLOC_MAX_ROWS, else FA_ERR_SCRATCH (nothing is enqueued). The array's
+ * address on the current device is looked up on the first call there (a HIP query,
+ * not an allocation). `stream` must belong to the current device. All calls on one GPU
+ * share that array and it keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that overlap in time on one GPU (different streams, or another
+ * thread) race on it and must be ordered by the caller.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   void* stream);
 
 /*
  * One stage of fa_bwd, same arguments plus `stage`, for callers that schedule or

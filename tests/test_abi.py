@@ -115,6 +115,25 @@ def test_bwd_validation_and_workspace(lib):
     assert lib.fa_bwd(*base, P, ws, 1, 2, 1, 8, 8, 80, 0.1, 1, None) == -4
 
 
+def test_bwd_noalloc_validation(lib):
+    """fa_bwd_noalloc: the same argument checks as fa_bwd, and B*Hq*Nq beyond its fixed
+    scratch is refused (FA_ERR_SCRATCH) before the library touches the HIP runtime."""
+    base = [P] * 9
+    assert lib.fa_bwd_noalloc(NULL, *base[1:], 1, 2, 1, 8, 8, 128, 0.1, 1, None) == -1
+    assert lib.fa_bwd_noalloc(*base[:8], NULL, 1, 2, 1, 8, 8, 128, 0.1, 1, None) == -1
+    assert lib.fa_bwd_noalloc(*base[:4], PU, *base[5:], 1, 2, 1, 8, 8, 128, 0.1, 1, None) == -5
+    assert lib.fa_bwd_noalloc(*base, 1, 3, 2, 8, 8, 128, 0.1, 1, None) == -3
+    assert lib.fa_bwd_noalloc(*base, 1, 2, 1, 8, 8, 80, 0.1, 1, None) == -4
+    assert lib.fa_bwd_noalloc(*base, 1, 2, 1, 0, 8, 128, 0.1, 1, None) == -2
+    assert lib.fa_bwd_noalloc(*base, 1, 2, 1, 8, 8, 128, 0.0, 1, None) == -10
+    rows = fa.BWD_NOALLOC_MAX_ROWS
+    assert lib.fa_bwd_noalloc(*base, 1, 1, 1, rows + 1, 8, 64, 0.1, 1, None) == -13
+    assert lib.fa_bwd_noalloc(*base, 4, 8, 8, rows // 32 + 1, 8, 64, 0.1, 0, None) == -13
+    assert "FA_BWD_NOALLOC_MAX_ROWS" in lib.fa_status_string(-13).decode()
+    hdr = open(HEADER).read()
+    assert f"#define FA_BWD_NOALLOC_MAX_ROWS {rows}" in hdr
+
+
 def test_bwd_stage_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 1, 8, 8, 128)
     args = [P] * 9 + [P, ws, 1, 2, 1, 8, 8, 128, 0.1, 1, None]
