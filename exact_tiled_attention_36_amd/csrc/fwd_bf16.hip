@@ -1,7 +1,8 @@
-// Forward attention, bf16: launches of the kernel in fwd_bf16.h for every head size
-// (8-wave workgroups, or 4 waves at d = 256) and the first-version comparison forms;
-// small grids go to fwd_bf16_small.hip.
+// Forward attention, bf16: launches of the software-pipelined kernel in fwd_bf16.h
+// (d = 64, 128: 8-wave workgroups) and of the two-group kernel in fwd_pp.h (d = 256), and
+// the first-version comparison forms; small grids go to fwd_bf16_small.hip.
 #include "fwd_bf16.h"
+#include "fwd_pp.h"
 
 namespace fa {
 namespace {
@@ -28,6 +29,12 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   if (wg256 < kSmallGrid && (s.d == 64 || s.d == 128)) {
     return launch_fwd_bf16_small(p, s.B, s.d, c, st);
   }
+  // d = 256: the two wave groups take turns on the matrix cores (fwd_pp.h), two waves
+  // per SIMD; measured 1.7x the one-wave-per-SIMD software-pipelined kernel (B2 H16
+  // N4096 causal: 490 -> 285 us). At d <= 128 a key tile's softmax takes about as long
+  // as its products, and the software-pipelined kernel below is 6-7 % faster.
+  if (s.d == 256)
+    return c ? run_pp<256, 32, true>(p, s.B, st) : run_pp<256, 32, false>(p, s.B, st);
   switch (s.d) {
 #ifndef FWD_CFG128
 #define FWD_CFG128 64, 8, 1
@@ -37,10 +44,6 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
 #endif
     case 64: return c ? run<64, FWD_CFG64, true>(p, s.B, st) : run<64, FWD_CFG64, false>(p, s.B, st);
     case 128: return c ? run<128, FWD_CFG128, true>(p, s.B, st) : run<128, FWD_CFG128, false>(p, s.B, st);
-#ifndef FWD_CFG256
-#define FWD_CFG256 32, 4, 1
-#endif
-    case 256: return c ? run<256, FWD_CFG256, true>(p, s.B, st) : run<256, FWD_CFG256, false>(p, s.B, st);
     default: return hipErrorInvalidValue;
   }
 }

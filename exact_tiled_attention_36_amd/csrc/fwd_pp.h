@@ -1,0 +1,325 @@
+// Forward attention, bf16, with two wave groups that take turns on the matrix cores
+// ("ping-pong"), for gfx950.
+//
+// Same method and result as fwd_bf16.h ("FlashAttention" (ruizhehou.github.io): tiles
+// of Q rows in the outer loop and of K/V in the inner loop, §二.1 and §三; running row
+// max and row sum with the rescale factor exp(m_old - m_new), §二.2; the output divided
+// by the row sum once at the end, §四.1; row blocks of a head in separate workgroups,
+// §四.2). What differs is how the work of one workgroup is laid out in time.
+//
+// A workgroup has 8 waves of 32 query rows; waves 0-3 form group A and waves 4-7
+// group B, so every SIMD holds one wave of each group. A wave's key-tile step has a
+// matrix phase (S_{t+1} = K_{t+1} Q^T, then O^T += V_t^T P_t^T: 32 products at d = 128)
+// and a vector phase (mask, row max, lazy rescale of O, exponentials, row sums and bf16
+// packing of S_{t+1} into P_{t+1}). The two groups are half a step apart: while the
+// wave of group A on a SIMD runs its matrix phase, the wave of group B runs its vector
+// phase, then they swap. On gfx950 a vector-only wave and a matrix-only wave on one
+// SIMD overlap (measured: paired they take 65 % of the sum of their separate times),
+// so each SIMD's matrix unit is fed by one wave while the other wave's softmax runs
+// beside it. A wave in its matrix phase raises its issue priority (s_setprio) so that
+// its products never wait behind the other wave's vector instructions.
+//
+// Phases are separated by workgroup barriers (two per key tile). K and V tiles are
+// double buffered in LDS: K_{t+1} and V_t are read by group A in the first phase of
+// step t and by group B in the second; the copies of K_{t+2} and V_{t+1} are issued at
+// the start of step t into the buffers that K_t and V_{t-1} left, and waited for at the
+// step's end barrier. Each wave needs only one score tile and one packed-weight tile
+// in registers (no in-wave software pipeline), which is what lets d = 256 run two waves
+// per SIMD here.
+#pragma once
+#include "fwd_bf16.h"
+
+#ifndef FWD_PP_LOOK
+#define FWD_PP_LOOK 4
+#endif
+
+namespace fa {
+namespace {
+
+// Scheduling hint for a run of NS products that read one LDS operand each followed by
+// NP products that read two: the reads are issued LOOK ahead of the products that use
+// them (sched_group_barrier groups, in program order).
+template <int LOOK, int NS, int NP>
+struct ReadAhead {
+  static constexpr int NR = NS + 2 * NP;
+  // reads wanted once product i has been issued
+  static constexpr int want(int i) {
+    const int need = i < 0 ? 0 : (i < NS ? i + 1 : NS + 2 * (i + 1 - NS));
+    return need + LOOK < NR ? need + LOOK : NR;
+  }
+  template <int I>
+  __device__ __forceinline__ static void one() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix product
+    if constexpr (want(I) > want(I - 1))
+      __builtin_amdgcn_sched_group_barrier(0x100, want(I) - want(I - 1), 0);  // LDS reads
+  }
+  template <int... I>
+  __device__ __forceinline__ static void all(std::integer_sequence<int, I...>) {
+    (one<I>(), ...);
+  }
+  __device__ __forceinline__ static void emit() {
+    __builtin_amdgcn_sched_group_barrier(0x100, want(-1), 0);
+    all(std::make_integer_sequence<int, NS + NP>());
+  }
+};
+
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
+  using TL = TileLayout<D>;
+  constexpr int NW = 8;
+  constexpr int BM = 32 * NW;    // query rows per workgroup
+  constexpr int TILE = TL::elems(BN);
+  constexpr int NKB = BN / 32;   // 32-key blocks per tile
+  constexpr int NDC = D / 16;    // 16-wide chunks of d (reduction of S)
+  constexpr int NCB = D / 32;    // 32-wide column blocks of O
+  static_assert(TL::shifts_ok(BN), "LDS reads add row offsets as constants");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp_b = wu >= 4;   // wave-uniform
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  int qb, bh;
+  if (CAUSAL) {
+    causal_order<2>(blockIdx.x, gridDim.x, p.nqb, bh, qb);
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    qb = L % p.nqb;
+    bh = L / p.nqb;
+  }
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int kvh = h / p.g;
+  const int q0 = qb * BM;
+  const int w0 = q0 + 32 * wu;  // first query row of this wave
+
+  const uint16_t* Qg = p.q + (size_t)(b * p.Hq + h) * p.Nq * D;
+  const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+  const uint16_t* Vg = p.v + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
+
+  bf16x8_t qreg[NDC];
+  {
+    const int qrow = w0 + l32;
+    const int qr = qrow < p.Nq ? qrow : p.Nq - 1;
+    const u32x4_t* src = (const u32x4_t*)(Qg + (size_t)qr * D + 8 * hi);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8_t, src[2 * dc]);
+  }
+  // nothing may be outstanding in the loop below except the tile copies it issues
+  wait_vmem();
+
+  int kend = p.Nk;
+  if (CAUSAL) {
+    const int lim = q0 + BM + p.causal_off;  // keys < lim may be visible to some row
+    kend = lim < kend ? lim : kend;
+  }
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // tiles [0, tfull) are wholly visible to every row of the workgroup
+  int tfull = p.Nk / BN;
+  if (CAUSAL) {
+    const int lim = q0 + p.causal_off + 1;  // keys < lim are visible to every row
+    tfull = min(tfull, lim > 0 ? lim / BN : 0);
+  }
+  tfull = min(tfull, ntiles);
+
+  f32x16_t oacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = zero16();
+  float m = -INFINITY, lsum = 0.f, m_use = 0.f, alpha = 1.f;
+  const float c2 = p.scale_log2;
+
+  auto Kb = [&](int i) FA_INLINE { return smem + (i & 1) * TILE; };
+  auto Vb = [&](int i) FA_INLINE { return smem + (2 + (i & 1)) * TILE; };
+  // Rows past the last key re-read the last key row: always finite, and masked to
+  // zero weight before they can contribute.
+  const uint32_t lane_off = 4u * lane;
+  auto load8 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
+    if constexpr (D <= 128) {
+      if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
+        tile_load_full<D, BN, 8>(G, t * BN, dst, wu, lane_off);
+        return;
+      }
+    }
+    tile_load_async<D, BN, 8>(G, t * BN, p.Nk, dst, wu, lane);
+  };
+  auto load4 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {  // group A only
+    if constexpr (D <= 128) {
+      if ((t + 1) * BN <= p.Nk) {
+        tile_load_full<D, BN, 4>(G, t * BN, dst, wu, lane_off);
+        return;
+      }
+    }
+    tile_load_async<D, BN, 4>(G, t * BN, p.Nk, dst, wu, lane);
+  };
+
+  // per-lane LDS byte offsets inside a tile: K operand rows, V^T transposed reads
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint32_t srow = 2 * (TL::row(l32) + 8 * hi);
+  const uint32_t trow = 2 * (TL::row(tr_row) + tr_col);
+
+  f32x16_t S[NKB];
+  uint32_t pk[NKB][8];
+
+  // S^T = K Q^T for one tile of BN keys
+  auto compute_s = [&](const uint16_t* Ks) FA_INLINE {
+    const uint32_t base = opaque(lds_addr(Ks) + srow);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) S[kb] = zero16();
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8_t a = lds_read8_at(base + 2 * (TL::row(32 * kb) + 16 * dc));
+        S[kb] = mfma32x32x16(a, qreg[dc], S[kb]);
+      }
+  };
+  // O^T += V^T P^T for one tile
+  auto pv = [&](const uint16_t* Vs) FA_INLINE {
+    const uint32_t base = opaque(lds_addr(Vs) + trow);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4_t bu = {pk[kb][4 * kk], pk[kb][4 * kk + 1], pk[kb][4 * kk + 2],
+                            pk[kb][4 * kk + 3]};
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bu);
+        const int R = 32 * kb + 16 * kk;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const bf16x8_t a = join8(lds_read_tr4_at(base + 2 * (TL::row(R) + 32 * cb)),
+                                   lds_read_tr4_at(base + 2 * (TL::row(R + 8) + 32 * cb)));
+          oacc[cb] = mfma32x32x16(a, bop, oacc[cb]);
+        }
+      }
+  };
+  // Matrix phase of step t: S_{t+1} (NEXT: there is a next tile), then O += V_t P_t.
+  // The LDS operand reads are kept a few reads ahead of the products that use them
+  // (left to itself the compiler hoists all of them and runs out of registers).
+  auto mat_phase = [&](int t, auto next_tag, auto pv_tag) FA_INLINE {
+    constexpr bool NEXT = decltype(next_tag)::value, PV = decltype(pv_tag)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (NEXT) compute_s(Kb(t + 1));
+    if constexpr (PV) pv(Vb(t));
+    ReadAhead<FWD_PP_LOOK, NEXT ? NDC * NKB : 0, PV ? 2 * NKB * NCB : 0>::emit();
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // vector phase: S_j (in S) into P_j (in pk), with m, l and the lazy rescale of O
+  auto vec_phase = [&](int j) FA_INLINE {
+    if (j >= tfull) {  // causal diagonal or key tail
+      const int j0 = j * BN;
+      const int lim = CAUSAL ? w0 + l32 + p.causal_off : 0x7fffffff;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= p.Nk || key > lim) S[kb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+    mx = xhalf_max(mx) * c2;
+    // the base moves only when some row's max passes it by more than the slack
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_next = fmaxf(m, mx);
+      m_use = (m_next == -INFINITY) ? 0.f : m_next;
+      alpha = fast_exp2(m - m_use);  // 0 on first use
+      m = m_next;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      lsum *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(S[kb][r], c2, -m_use));
+        const float p1 = fast_exp2(fmaf(S[kb][r + 1], c2, -m_use));
+        rs += p0 + p1;
+        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+      }
+    lsum += rs;
+  };
+  // Both groups run the same instruction stream; group B passes one extra barrier at
+  // the start and group A one at the end, which puts B half a step behind A. Barrier
+  // k of one group is barrier k of the other, so between two barriers one group runs
+  // a matrix phase while the other runs a vector phase. Group A issues every tile copy
+  // (at the start of its matrix phase of step t: K_{t+2} and V_{t+1}) and waits for
+  // them at the end of step t, before group A's next matrix phase and before group
+  // B's, which comes a phase later. Buffers: K_{t+1} and V_t are read by A in one phase
+  // and by B in the next; K_{t+2} replaces K_t and V_{t+1} replaces V_{t-1}, which B
+  // finished reading a phase before A issues the copies.
+  if (ntiles > 0) {
+    load8(Kg, 0, Kb(0));
+    if (ntiles > 1) load8(Kg, 1, Kb(1));
+    load8(Vg, 0, Vb(0));
+    wait_vmem();
+    __syncthreads();
+    if (grp_b) __syncthreads();
+    // S_0 and P_0
+    mat_phase(-1, BoolC<true>(), BoolC<false>());
+    __syncthreads();
+    vec_phase(0);
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < ntiles; ++t) {
+      if (!grp_b) {
+        if (t + 2 < ntiles) load4(Kg, t + 2, Kb(t));
+        load4(Vg, t + 1, Vb(t + 1));
+      }
+      mat_phase(t, BoolC<true>(), BoolC<true>());
+      __syncthreads();
+      vec_phase(t + 1);
+      wait_vmem();
+      __syncthreads();
+    }
+    // last step: only O += V_t P_t
+    mat_phase(t, BoolC<false>(), BoolC<true>());
+    __syncthreads();
+    if (!grp_b) __syncthreads();
+  }
+
+  // Epilogue: combine the two half-row sums, normalise once, store O and LSE.
+  const int qrow = w0 + l32;
+  const float ltot = xhalf_sum(lsum);
+  if (qrow < p.Nq) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (hi == 0) {
+      p.lse[(size_t)(b * p.Hq + h) * p.Nq + qrow] =
+          ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
+    }
+    uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + qrow) * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = 32 * cb + 8 * rg + 4 * hi;
+        u32x2_t val = {pack_bf16x2(oacc[cb][4 * rg] * inv, oacc[cb][4 * rg + 1] * inv),
+                       pack_bf16x2(oacc[cb][4 * rg + 2] * inv, oacc[cb][4 * rg + 3] * inv)};
+        *(u32x2_t*)(orow + c0) = val;
+      }
+  }
+}
+
+template <int D, int BN, bool CAUSAL>
+hipError_t run_pp(FwdParams p, long long B, hipStream_t st) {
+  constexpr int BM = 256;
+  p.nqb = (p.Nq + BM - 1) / BM;
+  const long long nb = (long long)p.nqb * p.Hq * B;
+  if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL>), dim3((int)nb), dim3(512), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fa
