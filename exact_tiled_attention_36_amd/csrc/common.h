@@ -287,22 +287,23 @@ __device__ __forceinline__ void tile_load_async(const uint16_t* G, int j0, int n
 }
 
 // The same copy for a tile whose ROWS rows all exist (j0 + ROWS <= nrows), in fewer
-// instructions. L describes the LDS layout: L::RPP rows per 256-byte piece (contiguous
-// in global memory and in LDS) and L::row_bytes(r), the byte offset of row r. Piece i
-// of wave wu lies 256*(wu + NW*i) bytes past the tile's first row in global memory, so
-// one scalar base per 4 KiB serves every piece and the rest goes into the
-// instruction's immediate offset (which the hardware also adds to the LDS address, so
-// M0 is lowered by it); the LDS offset of piece i from the wave's first piece is the
-// same for every wave (checked at compile time), a constant added to M0. About three
-// scalar instructions per piece, no vector ones.
+// instructions. L describes the LDS layout in 256-byte pieces, which are contiguous in
+// global memory and in LDS: L::pieces(rows) pieces hold `rows` rows, and
+// L::piece_bytes(u) is the LDS byte offset of piece u. Piece i of wave wu lies
+// 256*(wu + NW*i) bytes past the tile's first row in global memory, so one scalar base
+// per 4 KiB serves every piece and the rest goes into the instruction's immediate
+// offset (which the hardware also adds to the LDS address, so M0 is lowered by it);
+// the LDS offset of piece i from the wave's first piece is the same for every wave
+// (checked at compile time), a constant added to M0. About three scalar instructions
+// per piece, no vector ones.
 template <class L, int ROWS, int NW>
 struct PieceCopy {
-  static constexpr int NSEG = ROWS / L::RPP;
+  static constexpr int NSEG = L::pieces(ROWS);
   static constexpr int NI = NSEG / NW;
   static_assert(NSEG % NW == 0, "pieces must split evenly over the waves");
   // byte offset in LDS of piece i of wave w, relative to the wave's first piece
   static constexpr int lds_off(int w, int i) {
-    return L::row_bytes((w + NW * i) * L::RPP) - L::row_bytes(w * L::RPP);
+    return L::piece_bytes(w + NW * i) - L::piece_bytes(w);
   }
   static constexpr bool wave_independent() {
     for (int i = 0; i < NI; ++i)
@@ -329,17 +330,21 @@ struct PieceCopy {
   __device__ __forceinline__ static void run(const void* row0, void* lds, int wu,
                                              uint32_t lane_off) {
     const char* g0 = (const char*)row0 + 256 * wu;
-    const uint32_t m0 = lds_addr(lds) + L::row_bytes(wu * L::RPP);
+    const uint32_t m0 = lds_addr(lds) + L::piece_bytes(wu);
     all(g0, lane_off, m0, std::make_integer_sequence<int, NI>());
   }
 };
 
-// Rows of a bf16 TileLayout<D> as PieceCopy sees them (d = 64 or 128).
+// A bf16 TileLayout<D> in 256-byte pieces: a row pair (d = 64), a row (d = 128) or
+// half a row (d = 256).
 template <int D>
 struct BfRows {
-  static_assert(D == 64 || D == 128, "one piece per row or row pair");
-  static constexpr int RPP = D == 64 ? 2 : 1;
-  static constexpr int row_bytes(int r) { return 2 * TileLayout<D>::row(r); }
+  static constexpr int pieces(int rows) { return rows * D / 128; }
+  static constexpr int piece_bytes(int u) {
+    if constexpr (D == 64) return 2 * TileLayout<D>::row(2 * u);
+    else if constexpr (D == 128) return 2 * TileLayout<D>::row(u);
+    else return 2 * TileLayout<D>::row(u / 2) + 256 * (u % 2);
+  }
 };
 
 // Whole bf16 tile: rows j0 .. j0+ROWS-1 of G, all present.
@@ -348,6 +353,33 @@ __device__ __forceinline__ void tile_load_full(const uint16_t* G, int j0, uint16
                                                uint32_t lane_off) {
   PieceCopy<BfRows<D>, ROWS, NW>::run(G + (size_t)j0 * D, lds, wu, lane_off);
 }
+
+// Scheduling hint for a run of NS products that read one LDS operand each followed by
+// NP products that read two: the reads are issued LOOK ahead of the products that use
+// them (sched_group_barrier groups, in program order).
+template <int LOOK, int NS, int NP>
+struct ReadAhead {
+  static constexpr int NR = NS + 2 * NP;
+  // reads wanted once product i has been issued
+  static constexpr int want(int i) {
+    const int need = i < 0 ? 0 : (i < NS ? i + 1 : NS + 2 * (i + 1 - NS));
+    return need + LOOK < NR ? need + LOOK : NR;
+  }
+  template <int I>
+  __device__ __forceinline__ static void one() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix product
+    if constexpr (want(I) > want(I - 1))
+      __builtin_amdgcn_sched_group_barrier(0x100, want(I) - want(I - 1), 0);  // LDS reads
+  }
+  template <int... I>
+  __device__ __forceinline__ static void all(std::integer_sequence<int, I...>) {
+    (one<I>(), ...);
+  }
+  __device__ __forceinline__ static void emit() {
+    __builtin_amdgcn_sched_group_barrier(0x100, want(-1), 0);
+    all(std::make_integer_sequence<int, NS + NP>());
+  }
+};
 
 // Wait until this wave's vector memory operations (including direct LDS loads) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -16,8 +16,8 @@
 // phase, then they swap. On gfx950 a vector-only wave and a matrix-only wave on one
 // SIMD overlap (measured: paired they take 65 % of the sum of their separate times),
 // so each SIMD's matrix unit is fed by one wave while the other wave's softmax runs
-// beside it. A wave in its matrix phase raises its issue priority (s_setprio) so that
-// its products never wait behind the other wave's vector instructions.
+// beside it. (Raising the matrix-phase wave's issue priority with s_setprio measured
+// no faster, so both waves keep the default priority.)
 //
 // Phases are separated by workgroup barriers (two per key tile). K and V tiles are
 // double buffered in LDS: K_{t+1} and V_t are read by group A in the first phase of
@@ -35,33 +35,6 @@
 
 namespace fa {
 namespace {
-
-// Scheduling hint for a run of NS products that read one LDS operand each followed by
-// NP products that read two: the reads are issued LOOK ahead of the products that use
-// them (sched_group_barrier groups, in program order).
-template <int LOOK, int NS, int NP>
-struct ReadAhead {
-  static constexpr int NR = NS + 2 * NP;
-  // reads wanted once product i has been issued
-  static constexpr int want(int i) {
-    const int need = i < 0 ? 0 : (i < NS ? i + 1 : NS + 2 * (i + 1 - NS));
-    return need + LOOK < NR ? need + LOOK : NR;
-  }
-  template <int I>
-  __device__ __forceinline__ static void one() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix product
-    if constexpr (want(I) > want(I - 1))
-      __builtin_amdgcn_sched_group_barrier(0x100, want(I) - want(I - 1), 0);  // LDS reads
-  }
-  template <int... I>
-  __device__ __forceinline__ static void all(std::integer_sequence<int, I...>) {
-    (one<I>(), ...);
-  }
-  __device__ __forceinline__ static void emit() {
-    __builtin_amdgcn_sched_group_barrier(0x100, want(-1), 0);
-    all(std::make_integer_sequence<int, NS + NP>());
-  }
-};
 
 template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
@@ -135,20 +108,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   // zero weight before they can contribute.
   const uint32_t lane_off = 4u * lane;
   auto load8 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
-    if constexpr (D <= 128) {
-      if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
-        tile_load_full<D, BN, 8>(G, t * BN, dst, wu, lane_off);
-        return;
-      }
+    if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
+      tile_load_full<D, BN, 8>(G, t * BN, dst, wu, lane_off);
+      return;
     }
     tile_load_async<D, BN, 8>(G, t * BN, p.Nk, dst, wu, lane);
   };
   auto load4 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {  // group A only
-    if constexpr (D <= 128) {
-      if ((t + 1) * BN <= p.Nk) {
-        tile_load_full<D, BN, 4>(G, t * BN, dst, wu, lane_off);
-        return;
-      }
+    if ((t + 1) * BN <= p.Nk) {
+      tile_load_full<D, BN, 4>(G, t * BN, dst, wu, lane_off);
+      return;
     }
     tile_load_async<D, BN, 4>(G, t * BN, p.Nk, dst, wu, lane);
   };
@@ -200,11 +169,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   auto mat_phase = [&](int t, auto next_tag, auto pv_tag) FA_INLINE {
     constexpr bool NEXT = decltype(next_tag)::value, PV = decltype(pv_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
     if constexpr (NEXT) compute_s(Kb(t + 1));
     if constexpr (PV) pv(Vb(t));
     ReadAhead<FWD_PP_LOOK, NEXT ? NDC * NKB : 0, PV ? 2 * NKB * NCB : 0>::emit();
-    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
   // vector phase: S_j (in S) into P_j (in pk), with m, l and the lazy rescale of O
