@@ -50,12 +50,24 @@ hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (stage == -1 || stage == 1) {
-    const int nkb = (p.Nk + 127) / 128;
+    // Grids of fewer than 256 workgroups of 128 keys leave compute units idle: there
+    // each workgroup takes 64 keys, its two wave pairs splitting every query tile
+    // (d = 64, 128).
+    const long long wg128 = (long long)((p.Nk + 127) / 128) * p.Hkv * B;
+    const bool split = BMQ == 64 && wg128 < 256;
+    const int bnk = split ? 64 : 128;
+    const int nkb = (p.Nk + bnk - 1) / bnk;
     const long long n = (long long)nkb * p.Hkv * B;
     if (n > 0x7fffffffLL) return hipErrorInvalidValue;
     hipError_t e;
     if constexpr (D == 128 && BMQ == 64) {
-      e = launch_bwd_dkdv_d128(p, nkb, (int)n, CAUSAL, st);
+      e = launch_bwd_dkdv_d128(p, nkb, (int)n, CAUSAL, split, st);
+    } else if constexpr (BMQ == 64) {
+      if (split)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, BMQ, CAUSAL, true>), dim3((int)n), dim3(256), 0, st, p, nkb);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, BMQ, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nkb);
+      e = hipGetLastError();
     } else {
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, BMQ, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nkb);
       e = hipGetLastError();

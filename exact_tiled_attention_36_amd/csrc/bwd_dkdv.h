@@ -24,8 +24,9 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
-// Launch of bwd_dkdv_kernel<128, 64, causal> on `grid` workgroups (bwd_dkdv_d128.hip).
-hipError_t launch_bwd_dkdv_d128(const BwdParams& p, int nkb, int grid, bool causal,
+// Launch of bwd_dkdv_kernel<128, 64, causal, split> on `grid` workgroups
+// (bwd_dkdv_d128.hip).
+hipError_t launch_bwd_dkdv_d128(const BwdParams& p, int nkb, int grid, bool causal, bool split,
                                 hipStream_t st);
 
 namespace {
@@ -57,12 +58,19 @@ struct BoolC {
 // one slice's S/dP accumulators are live at a time. The previous slice of a step's
 // first slice is the last slice of the step before, which is why tiles stay in LDS
 // for two steps. Each sub-phase also reads the LDS operands of the next one.
-template <int D, int BMQ, bool CAUSAL>
+//
+// SPLIT (grids too small to fill the GPU with 128-key workgroups): a workgroup covers
+// 64 keys; waves w and w+2 own the same 32 keys and take one 32-query slice each of
+// every tile (wave w+2 the upper one), and at the end wave w+2 hands its dK/dV partial
+// sums to wave w through LDS. Twice the workgroups for the same work, every SIMD busy.
+template <int D, int BMQ, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) {
   using TL = TileLayout<D>;
   constexpr int TILE = TL::elems(BMQ);
-  constexpr int NDC = D / 16, NCB = D / 32, NQS = BMQ / 32, HD = NDC / 2;
-  constexpr int BNK = 128, NB = 3;
+  constexpr int NDC = D / 16, NCB = D / 32, HD = NDC / 2;
+  static_assert(!SPLIT || BMQ == 64, "split slices need two 32-query slices per tile");
+  constexpr int NQS = SPLIT ? 1 : BMQ / 32;  // query slices per wave and tile
+  constexpr int BNK = SPLIT ? 64 : 128, NB = 3;
   constexpr int SV = BMQ < 64 ? 64 : BMQ;  // statistics slots per buffer and kind
   static_assert(SV % 64 == 0, "statistics rows per step");
 
@@ -84,7 +92,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   }
   const int kvh = bkv % p.Hkv, b = bkv / p.Hkv;
   const int k0 = kb * BNK;
-  const int key = k0 + 32 * w + l32;
+  const int key = k0 + 32 * (SPLIT ? (w & 1) : w) + l32;
+  const int qoff = SPLIT ? 32 * (wu >> 1) : 0;  // this wave's slice within a tile
 
   bf16x8_t kreg[NDC], vreg[NDC];
   {
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
   static_assert(TL::shifts_ok(BMQ), "LDS reads add row offsets as constants");
   // byte address of this lane's transposed reads in a Q tile (dO: + 2*TILE bytes)
   auto tr_base = [&](const uint16_t* T) FA_INLINE {
-    return opaque(lds_addr(T) + 2 * (TL::row(tr_row) + tr_col));
+    return opaque(lds_addr(T) + 2 * (TL::row(tr_row + qoff) + tr_col));
   };
   // dV += dO^T P, dK += Q^T dS for rows 16kk.. of slice `sl` of the tile at tb
   auto rd_g = [&](uint32_t tb, int sl, int kk, bf16x8_t* ga, bf16x8_t* gb) FA_INLINE {
@@ -283,9 +292,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     const uint16_t* Qs = qtile(s);
     const uint16_t* Qp = s > 0 ? qtile(s - 1) : Qs;  // with P = dS = 0 at s = 0
     // per-lane LDS byte bases of this step's reads (constants are added to them)
-    const uint32_t sbase = opaque(lds_addr(Qs) + 2 * TL::row(l32) + 16 * hi);
+    const uint32_t sbase = opaque(lds_addr(Qs) + 2 * TL::row(l32 + qoff) + 16 * hi);
     const uint32_t tcur = tr_base(Qs), tprev = tr_base(Qp);
-    const uint32_t lbase = opaque(lds_addr(stats(s)) + 16 * hi);
+    const uint32_t lbase = opaque(lds_addr(stats(s)) + 16 * hi + 4 * qoff);
 
     bf16x8_t sa[2][HD], sb[2][HD];    // Q and dO row operands of an S/dP sub-phase
     bf16x8_t ga[2][NCB], gb[2][NCB];  // dO^T and Q^T operands of a dV/dK sub-phase
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
           const int r = 4 * rg + e;
           float pr = fast_exp2(fmaf(S[r], c2, -lv[kk][rr][e]));
           if (MASK) {
-            const int i = i0 + 32 * qs + 8 * rg + 4 * hi + e;
+            const int i = i0 + qoff + 32 * qs + 8 * rg + 4 * hi + e;
             if ((CAUSAL && key > i + p.causal_off) || i >= p.Nq) pr = 0.f;
           }
           pv[e] = pr;
@@ -438,6 +447,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     }
   }
 
+  if constexpr (SPLIT) {
+    // waves 2, 3 hand their partial sums to waves 0, 1 (the tiles are no longer read)
+    __syncthreads();
+    f32x16_t* xfer = (f32x16_t*)smem + ((w & 1) * 2 * NCB) * 64 + lane;
+    if (wu >= 2) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        xfer[cb * 64] = dkacc[cb];
+        xfer[(NCB + cb) * 64] = dvacc[cb];
+      }
+    }
+    __syncthreads();
+    if (wu >= 2) return;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      dkacc[cb] += xfer[cb * 64];
+      dvacc[cb] += xfer[(NCB + cb) * 64];
+    }
+  }
   if (key < p.Nk) {
     const size_t base = ((size_t)(b * p.Hkv + kvh) * p.Nk + key) * D;
 #pragma unroll

@@ -13,12 +13,18 @@
 
 namespace fa {
 
-hipError_t launch_bwd_dkdv_d128(const BwdParams& p, int nkb, int grid, bool causal,
+hipError_t launch_bwd_dkdv_d128(const BwdParams& p, int nkb, int grid, bool causal, bool split,
                                 hipStream_t st) {
-  if (causal)
+  if (split) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, 64, true, true>), dim3(grid), dim3(256), 0, st, p, nkb);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, 64, false, true>), dim3(grid), dim3(256), 0, st, p, nkb);
+  } else if (causal) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<128, 64, true>), dim3(grid), dim3(256), 0, st, p, nkb);
-  else
+  } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<128, 64, false>), dim3(grid), dim3(256), 0, st, p, nkb);
+  }
   return hipGetLastError();
 }
 
