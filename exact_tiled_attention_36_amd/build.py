@@ -19,6 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+# Debug build: every kernel step also waits for its copies and passes a workgroup
+# barrier (csrc/common.h debug_sync); its results must match libfa.so bit for bit.
+SYNC_LIB = os.path.join(PKG, "libfa_sync.so")
+SYNC_FLAGS = ("-DFA_DEBUG_BARRIERS=1",)
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for all device code (see DESIGN notes);

@@ -370,6 +370,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     rd_s(0, 0);
     issue_next();
     __builtin_amdgcn_sched_barrier(0);
+    debug_sync();
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       // previous slice: the last one of the step before, or qs-1 of this step
@@ -403,6 +404,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       pprev[kk] = pc[NQS - 1][kk];
       dprev[kk] = dsc[NQS - 1][kk];
     }
+    debug_sync();
   };
 
   Cur cur = {0, 0, 0};

@@ -205,11 +205,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
     constexpr bool MASK = decltype(mask_tag)::value, LAST = decltype(last_tag)::value;
     if constexpr (!LAST) load_tile(t + 2);  // into the buffer of tile t-1, done with
     __builtin_amdgcn_sched_barrier(0);
+    debug_sync();
     if constexpr (!LAST) compute_sp(sn, pn, t + 1);
     dsoft(sc, pc, dspk);
     dq_mm(dspk, t);
     if constexpr (!LAST && MASK) mask(sn, t + 1);
     __builtin_amdgcn_sched_barrier(0);
+    debug_sync();
     if constexpr (!LAST) {
       wait_vmem();
       __syncthreads();

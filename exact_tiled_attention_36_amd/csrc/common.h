@@ -384,6 +384,21 @@ struct ReadAhead {
 // Wait until this wave's vector memory operations (including direct LDS loads) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Debug build (FA_DEBUG_BARRIERS=1, built as libfa_sync.so): every kernel step also
+// completes its copies and passes a workgroup barrier at the points that call this.
+// Barriers change only timing, so its results must equal the normal build's bit for
+// bit; a difference means some LDS access is not ordered by the kernel's own waits
+// and barriers (a race). Every wave of a workgroup calls it the same number of times.
+#ifndef FA_DEBUG_BARRIERS
+#define FA_DEBUG_BARRIERS 0
+#endif
+__device__ __forceinline__ void debug_sync() {
+  if constexpr (FA_DEBUG_BARRIERS != 0) {
+    wait_vmem();
+    __syncthreads();
+  }
+}
+
 // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2). Map the
 // hardware id to a logical id so that consecutive logical ids run on one XCD.
 __host__ __device__ __forceinline__ int xcd_remap(int hw, int n) {

@@ -329,6 +329,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_fp8_kernel(Fp8Params p) {
       load(Vg, t + 1, Vb(t + 1));
     }
     __builtin_amdgcn_sched_barrier(0);
+    debug_sync();
     if constexpr (!LAST) compute_s(nxt, Kb(t + 1));
     sexp(cur, pk);
     pv(pk, Vb(t));
@@ -337,6 +338,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_fp8_kernel(Fp8Params p) {
       move = smax(nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
+    debug_sync();
     if constexpr (!LAST) {
       wait_vmem();
       __syncthreads();

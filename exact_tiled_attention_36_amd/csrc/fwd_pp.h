@@ -169,6 +169,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   auto mat_phase = [&](int t, auto next_tag, auto pv_tag) FA_INLINE {
     constexpr bool NEXT = decltype(next_tag)::value, PV = decltype(pv_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
+    debug_sync();
     if constexpr (NEXT) compute_s(Kb(t + 1));
     if constexpr (PV) pv(Vb(t));
     ReadAhead<FWD_PP_LOOK, NEXT ? NDC * NKB : 0, PV ? 2 * NKB * NCB : 0>::emit();
