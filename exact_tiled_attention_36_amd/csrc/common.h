@@ -354,15 +354,16 @@ __device__ __forceinline__ void tile_load_full(const uint16_t* G, int j0, uint16
   PieceCopy<BfRows<D>, ROWS, NW>::run(G + (size_t)j0 * D, lds, wu, lane_off);
 }
 
-// Scheduling hint for a run of NS products that read one LDS operand each followed by
-// NP products that read two: the reads are issued LOOK ahead of the products that use
-// them (sched_group_barrier groups, in program order).
-template <int LOOK, int NS, int NP>
-struct ReadAhead {
-  static constexpr int NR = NS + 2 * NP;
+// Scheduling hint for a run of N1 operand groups of R1 LDS reads followed by N2 groups
+// of R2 reads, each group feeding QB consecutive products: the reads are issued LOOK
+// ahead of the products that use them (sched_group_barrier groups, in program order).
+template <int LOOK, int N1, int R1, int N2, int R2, int QB = 1>
+struct ReadAheadG {
+  static constexpr int NR = R1 * N1 + R2 * N2;
   // reads wanted once product i has been issued
   static constexpr int want(int i) {
-    const int need = i < 0 ? 0 : (i < NS ? i + 1 : NS + 2 * (i + 1 - NS));
+    const int need =
+        i < 0 ? 0 : (i < QB * N1 ? R1 * (i / QB + 1) : R1 * N1 + R2 * ((i - QB * N1) / QB + 1));
     return need + LOOK < NR ? need + LOOK : NR;
   }
   template <int I>
@@ -377,9 +378,12 @@ struct ReadAhead {
   }
   __device__ __forceinline__ static void emit() {
     __builtin_amdgcn_sched_group_barrier(0x100, want(-1), 0);
-    all(std::make_integer_sequence<int, NS + NP>());
+    all(std::make_integer_sequence<int, QB * (N1 + N2)>());
   }
 };
+// NS products that read one LDS operand each, then NP that read two
+template <int LOOK, int NS, int NP>
+using ReadAhead = ReadAheadG<LOOK, NS, 1, NP, 2, 1>;
 
 // Wait until this wave's vector memory operations (including direct LDS loads) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

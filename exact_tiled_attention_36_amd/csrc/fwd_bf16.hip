@@ -1,6 +1,7 @@
 // Forward attention, bf16: launches of the software-pipelined kernel in fwd_bf16.h
-// (d = 64, 128: 8-wave workgroups) and of the two-group kernel in fwd_pp.h (d = 256), and
-// the first-version comparison forms; small grids go to fwd_bf16_small.hip.
+// (d = 64, and d = 128 for shorter sequences: 8-wave workgroups) and of the two-group
+// kernel in fwd_pp.h (d = 256, and d = 128 for long sequences), and the first-version
+// comparison forms; small grids go to fwd_bf16_small.hip.
 #include "fwd_bf16.h"
 #include "fwd_pp.h"
 
@@ -11,6 +12,10 @@ namespace {
 #define FWD_SMALL_GRID 256
 #endif
 constexpr long long kSmallGrid = FWD_SMALL_GRID;
+#ifndef FWD_PP128_MIN_ROWS
+#define FWD_PP128_MIN_ROWS 4096
+#endif
+constexpr int kPp128MinRows = FWD_PP128_MIN_ROWS;
 
 }  // namespace
 
@@ -35,6 +40,16 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   // as its products, and the software-pipelined kernel below is 6-7 % faster.
   if (s.d == 256)
     return c ? run_pp<256, 32, true>(p, s.B, st) : run_pp<256, 32, false>(p, s.B, st);
+  // d = 128, long query sequences (4096 rows non-causal, 8192 causal): the two-group
+  // kernel with 64 rows per wave (fwd_pp.h, 512-row workgroups), when that still gives
+  // every compute unit a workgroup. Each K / V^T operand read from LDS then feeds two
+  // products. Time against the kernel below: B1 H8 N32768 causal -8 %, B2 Hq32 Hkv8
+  // N8192 causal -6.5 %, B2 H32 N4096 and B1 H8 N16384 non-causal -9 %; but B4 H32
+  // N4096 causal +1 %: there a 512-row workgroup walks the diagonal tiles for all of its
+  // rows, a larger share of the work.
+  const long long wg512 = (long long)((s.Nq + 511) / 512) * s.Hq * s.B;
+  if (s.d == 128 && s.Nq >= (c ? 2 * kPp128MinRows : kPp128MinRows) && wg512 >= kSmallGrid)
+    return c ? run_pp<128, 32, true, 2>(p, s.B, st) : run_pp<128, 32, false, 2>(p, s.B, st);
   switch (s.d) {
 #ifndef FWD_CFG128
 #define FWD_CFG128 64, 8, 1

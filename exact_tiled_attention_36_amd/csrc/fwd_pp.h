@@ -7,25 +7,36 @@
 // by the row sum once at the end, §四.1; row blocks of a head in separate workgroups,
 // §四.2). What differs is how the work of one workgroup is laid out in time.
 //
-// A workgroup has 8 waves of 32 query rows; waves 0-3 form group A and waves 4-7
-// group B, so every SIMD holds one wave of each group. A wave's key-tile step has a
-// matrix phase (S_{t+1} = K_{t+1} Q^T, then O^T += V_t^T P_t^T: 32 products at d = 128)
-// and a vector phase (mask, row max, lazy rescale of O, exponentials, row sums and bf16
-// packing of S_{t+1} into P_{t+1}). The two groups are half a step apart: while the
-// wave of group A on a SIMD runs its matrix phase, the wave of group B runs its vector
-// phase, then they swap. On gfx950 a vector-only wave and a matrix-only wave on one
-// SIMD overlap (measured: paired they take 65 % of the sum of their separate times),
-// so each SIMD's matrix unit is fed by one wave while the other wave's softmax runs
-// beside it. (Raising the matrix-phase wave's issue priority with s_setprio measured
-// no faster, so both waves keep the default priority.)
+// A workgroup has 8 waves of QB blocks of 32 query rows; waves 0-3 form group A and
+// waves 4-7 group B, so every SIMD holds one wave of each group. A wave's key-tile
+// step has a matrix phase (S_{t+1} = K_{t+1} Q^T and O^T += V_t^T P_t^T) and a vector
+// phase (mask, row max, lazy rescale of O, exponentials, row sums and bf16 packing of
+// S_{t+1} into P_{t+1}). The two groups are half a step apart: while the wave of group
+// A on a SIMD runs its matrix phase, the wave of group B runs its vector phase, then
+// they swap. On gfx950 a vector-only wave and a matrix-only wave on one SIMD overlap
+// (measured: paired they take 65 % of the sum of their separate times), so each SIMD's
+// matrix unit is fed by one wave while the other wave's softmax runs beside it.
+// (Raising the matrix-phase wave's issue priority with s_setprio measured no faster,
+// so both waves keep the default priority.)
 //
 // Phases are separated by workgroup barriers (two per key tile). K and V tiles are
 // double buffered in LDS: K_{t+1} and V_t are read by group A in the first phase of
 // step t and by group B in the second; the copies of K_{t+2} and V_{t+1} are issued at
 // the start of step t into the buffers that K_t and V_{t-1} left, and waited for at the
 // step's end barrier. Each wave needs only one score tile and one packed-weight tile
-// in registers (no in-wave software pipeline), which is what lets d = 256 run two waves
-// per SIMD here.
+// per query block in registers (no in-wave software pipeline).
+//
+// QB = 1 (d = 256): 32 rows per wave, Q in registers.
+// QB = 2 (d = 128, large grids): 64 rows per wave, 512 per workgroup, so every K or
+// V^T operand read from LDS feeds two products instead of one (LDS bytes per product
+// 0.75 KB instead of 1 KB at d = 128, and half as many workgroups for the same rows).
+// The registers (256 per wave at two waves per SIMD) hold Q of the first block and
+// the 128 output accumulators; the second block's Q rows sit in a tile of the wave's
+// own in LDS. With this many live accumulators the loop must have a single producer
+// of O: every key tile, the last included, runs through one loop (the last step's
+// scores come from a stale buffer and are never used). The form with a separate last
+// step made the compiler keep a second copy of O across the loop and spill.
+#pragma once
 #pragma once
 #include "fwd_bf16.h"
 
@@ -36,18 +47,27 @@
 namespace fa {
 namespace {
 
-template <int D, int BN, bool CAUSAL>
+// starting value of the running max: finite, so a row that has seen no key yet needs
+// no special case (its weights are exp2(-inf) = 0, its first rescale factor 0)
+constexpr float kNoMax = -1e30f;
+
+template <int D, int BN, bool CAUSAL, int QB>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   constexpr int NW = 8;
-  constexpr int BM = 32 * NW;    // query rows per workgroup
+  constexpr int RW = 32 * QB;    // query rows per wave (QB blocks of 32)
+  constexpr int BM = RW * NW;    // query rows per workgroup
   constexpr int TILE = TL::elems(BN);
   constexpr int NKB = BN / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide chunks of d (reduction of S)
   constexpr int NCB = D / 32;    // 32-wide column blocks of O
   static_assert(TL::shifts_ok(BN), "LDS reads add row offsets as constants");
+  static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
+  // with two blocks, the second block's Q rows stay in LDS (a tile per wave): the
+  // registers hold Q of the first block only
+  constexpr int QT = TL::elems(32);
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (QB - 1) * NW * QT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -65,7 +85,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.g;
   const int q0 = qb * BM;
-  const int w0 = q0 + 32 * wu;  // first query row of this wave
+  const int w0 = q0 + RW * wu;  // first query row of this wave
 
   const uint16_t* Qg = p.q + (size_t)(b * p.Hq + h) * p.Nq * D;
   const uint16_t* Kg = p.k + (size_t)(b * p.Hkv + kvh) * p.Nk * D;
@@ -79,6 +99,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8_t, src[2 * dc]);
   }
+  uint16_t* const q1t = smem + 4 * TILE + wu * QT;  // this wave's second Q block (QB = 2)
+  if constexpr (QB == 2) tile_load_async<D, 32, 1>(Qg, w0 + 32, p.Nq, q1t, 0, lane);
   // nothing may be outstanding in the loop below except the tile copies it issues
   wait_vmem();
 
@@ -96,10 +118,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   }
   tfull = min(tfull, ntiles);
 
-  f32x16_t oacc[NCB];
+  f32x16_t oacc[QB][NCB];
+  float m[QB], lsum[QB];  // running max (log2 units) and row sum per block
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = zero16();
-  float m = -INFINITY, lsum = 0.f, m_use = 0.f, alpha = 1.f;
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) oacc[qb][cb] = zero16();
+    m[qb] = kNoMax;
+    lsum[qb] = 0.f;
+  }
   const float c2 = p.scale_log2;
 
   auto Kb = [&](int i) FA_INLINE { return smem + (i & 1) * TILE; };
@@ -128,95 +155,130 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   const uint32_t srow = 2 * (TL::row(l32) + 8 * hi);
   const uint32_t trow = 2 * (TL::row(tr_row) + tr_col);
 
-  f32x16_t S[NKB];
-  uint32_t pk[NKB][8];
+  f32x16_t S[QB][NKB];
+  u32x4_t pk[QB][NKB][2];  // packed bf16 weights, one MFMA B operand per 16 keys
 
-  // S^T = K Q^T for one tile of BN keys
+  // S^T = K Q^T for one tile of BN keys; every K operand read feeds the QB blocks (the
+  // second block's Q^T operand is a 16-byte row read of its LDS tile)
   auto compute_s = [&](const uint16_t* Ks) FA_INLINE {
     const uint32_t base = opaque(lds_addr(Ks) + srow);
+    const uint32_t qbase = QB == 2 ? opaque(lds_addr(q1t) + srow) : 0u;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) S[kb] = zero16();
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) S[qb][kb] = zero16();
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8_t a = lds_read8_at(base + 2 * (TL::row(32 * kb) + 16 * dc));
-        S[kb] = mfma32x32x16(a, qreg[dc], S[kb]);
+        S[0][kb] = mfma32x32x16(a, qreg[dc], S[0][kb]);
+        if constexpr (QB == 2) {
+          const bf16x8_t q1 = lds_read8_at(qbase + 2 * 16 * dc);
+          S[1][kb] = mfma32x32x16(a, q1, S[1][kb]);
+        }
       }
   };
-  // O^T += V^T P^T for one tile
+  // O^T += V^T P^T for one tile; every V^T operand read feeds the QB blocks
   auto pv = [&](const uint16_t* Vs) FA_INLINE {
     const uint32_t base = opaque(lds_addr(Vs) + trow);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const u32x4_t bu = {pk[kb][4 * kk], pk[kb][4 * kk + 1], pk[kb][4 * kk + 2],
-                            pk[kb][4 * kk + 3]};
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bu);
+        bf16x8_t bop[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          bop[qb] = __builtin_bit_cast(bf16x8_t, pk[qb][kb][kk]);
+        }
         const int R = 32 * kb + 16 * kk;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const bf16x8_t a = join8(lds_read_tr4_at(base + 2 * (TL::row(R) + 32 * cb)),
                                    lds_read_tr4_at(base + 2 * (TL::row(R + 8) + 32 * cb)));
-          oacc[cb] = mfma32x32x16(a, bop, oacc[cb]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][cb] = mfma32x32x16(a, bop[qb], oacc[qb][cb]);
         }
       }
   };
-  // Matrix phase of step t: S_{t+1} (NEXT: there is a next tile), then O += V_t P_t.
+  // Matrix phase of step t: S_{t+1} (NEXT: there is a next tile) and O += V_t P_t.
   // The LDS operand reads are kept a few reads ahead of the products that use them
   // (left to itself the compiler hoists all of them and runs out of registers).
   auto mat_phase = [&](int t, auto next_tag, auto pv_tag) FA_INLINE {
     constexpr bool NEXT = decltype(next_tag)::value, PV = decltype(pv_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
     debug_sync();
-    if constexpr (NEXT) compute_s(Kb(t + 1));
-    if constexpr (PV) pv(Vb(t));
-    ReadAhead<FWD_PP_LOOK, NEXT ? NDC * NKB : 0, PV ? 2 * NKB * NCB : 0>::emit();
+    constexpr int NS = NEXT ? NDC * NKB : 0, NP = PV ? 2 * NKB * NCB : 0;
+    if constexpr (QB == 1) {
+      if constexpr (NEXT) compute_s(Kb(t + 1));
+      if constexpr (PV) pv(Vb(t));
+      ReadAheadG<FWD_PP_LOOK, NS, 1, NP, 2>::emit();
+    } else {
+      // O += V_t P_t first: the weights die before the next scores are made
+      if constexpr (PV) pv(Vb(t));
+      if constexpr (NEXT) compute_s(Kb(t + 1));
+      ReadAheadG<FWD_PP_LOOK, NP, 2, NS, 2, QB>::emit();
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   // vector phase: S_j (in S) into P_j (in pk), with m, l and the lazy rescale of O
   auto vec_phase = [&](int j) FA_INLINE {
     if (j >= tfull) {  // causal diagonal or key tail
-      const int j0 = j * BN;
-      const int lim = CAUSAL ? w0 + l32 + p.causal_off : 0x7fffffff;
+      // key j*BN + 4*hi + c (c a per-register constant) is visible to this lane's row
+      // iff c <= T, with T the last visible key less the lane's base
+      const int base = j * BN + 4 * hi;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        int last = p.Nk - 1;
+        if (CAUSAL) last = min(last, w0 + 32 * qb + l32 + p.causal_off);
+        const int T = last - base;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > T) S[qb][kb][r] = -INFINITY;
+      }
+    }
+    float mx[QB];
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      mx[qb] = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= p.Nk || key > lim) S[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) mx[qb] = fmaxf(mx[qb], S[qb][kb][r]);
+      mx[qb] = xhalf_max(mx[qb]) * c2;
+      up = up || mx[qb] > m[qb] + kRescaleSlack;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
-    mx = xhalf_max(mx) * c2;
     // the base moves only when some row's max passes it by more than the slack
-    if (__any(mx > m + kRescaleSlack)) {
-      const float m_next = fmaxf(m, mx);
-      m_use = (m_next == -INFINITY) ? 0.f : m_next;
-      alpha = fast_exp2(m - m_use);  // 0 on first use
-      m = m_next;
+    if (__any(up)) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_next = fmaxf(m[qb], mx[qb]);
+        const float alpha = fast_exp2(m[qb] - m_next);  // 0 on first use, 1 if unchanged
+        m[qb] = m_next;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-      lsum *= alpha;
-    }
-    float rs = 0.f;
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(S[kb][r], c2, -m_use));
-        const float p1 = fast_exp2(fmaf(S[kb][r + 1], c2, -m_use));
-        rs += p0 + p1;
-        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+          for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
+        lsum[qb] *= alpha;
       }
-    lsum += rs;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(S[qb][kb][r], c2, -m[qb]));
+          const float p1 = fast_exp2(fmaf(S[qb][kb][r + 1], c2, -m[qb]));
+          rs += p0 + p1;
+          pk[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+        }
+      lsum[qb] += rs;
+    }
   };
   // Both groups run the same instruction stream; group B passes one extra barrier at
   // the start and group A one at the end, which puts B half a step behind A. Barrier
@@ -239,53 +301,73 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
     __syncthreads();
     vec_phase(0);
     __syncthreads();
-    int t = 0;
-    for (; t + 1 < ntiles; ++t) {
-      if (!grp_b) {
-        if (t + 2 < ntiles) load4(Kg, t + 2, Kb(t));
-        load4(Vg, t + 1, Vb(t + 1));
+    if constexpr (QB == 2) {
+      // every step in one loop (the last one's scores are made from a stale buffer and
+      // never used), so the output accumulators have one producer in the loop
+      for (int t = 0; t < ntiles; ++t) {
+        if (!grp_b) {
+          if (t + 2 < ntiles) load4(Kg, t + 2, Kb(t));
+          if (t + 1 < ntiles) load4(Vg, t + 1, Vb(t + 1));
+        }
+        mat_phase(t, BoolC<true>(), BoolC<true>());
+        __syncthreads();
+        if (t + 1 < ntiles) vec_phase(t + 1);
+        wait_vmem();
+        __syncthreads();
       }
-      mat_phase(t, BoolC<true>(), BoolC<true>());
+      if (!grp_b) __syncthreads();
+    } else {
+      int t = 0;
+      for (; t + 1 < ntiles; ++t) {
+        if (!grp_b) {
+          if (t + 2 < ntiles) load4(Kg, t + 2, Kb(t));
+          load4(Vg, t + 1, Vb(t + 1));
+        }
+        mat_phase(t, BoolC<true>(), BoolC<true>());
+        __syncthreads();
+        vec_phase(t + 1);
+        wait_vmem();
+        __syncthreads();
+      }
+      // last step: only O += V_t P_t
+      mat_phase(t, BoolC<false>(), BoolC<true>());
       __syncthreads();
-      vec_phase(t + 1);
-      wait_vmem();
-      __syncthreads();
+      if (!grp_b) __syncthreads();
     }
-    // last step: only O += V_t P_t
-    mat_phase(t, BoolC<false>(), BoolC<true>());
-    __syncthreads();
-    if (!grp_b) __syncthreads();
   }
 
   // Epilogue: combine the two half-row sums, normalise once, store O and LSE.
-  const int qrow = w0 + l32;
-  const float ltot = xhalf_sum(lsum);
-  if (qrow < p.Nq) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (hi == 0) {
-      p.lse[(size_t)(b * p.Hq + h) * p.Nq + qrow] =
-          ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
-    }
-    uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + qrow) * D;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int c0 = 32 * cb + 8 * rg + 4 * hi;
-        u32x2_t val = {pack_bf16x2(oacc[cb][4 * rg] * inv, oacc[cb][4 * rg + 1] * inv),
-                       pack_bf16x2(oacc[cb][4 * rg + 2] * inv, oacc[cb][4 * rg + 3] * inv)};
-        *(u32x2_t*)(orow + c0) = val;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = w0 + 32 * qb + l32;
+    const float ltot = xhalf_sum(lsum[qb]);
+    if (qrow < p.Nq) {
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      if (hi == 0) {
+        p.lse[(size_t)(b * p.Hq + h) * p.Nq + qrow] =
+            ltot > 0.f ? (m[qb] + log2f(ltot)) * kLn2 : -INFINITY;
       }
+      uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + qrow) * D;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int c0 = 32 * cb + 8 * rg + 4 * hi;
+          u32x2_t val = {pack_bf16x2(oacc[qb][cb][4 * rg] * inv, oacc[qb][cb][4 * rg + 1] * inv),
+                         pack_bf16x2(oacc[qb][cb][4 * rg + 2] * inv, oacc[qb][cb][4 * rg + 3] * inv)};
+          *(u32x2_t*)(orow + c0) = val;
+        }
+    }
   }
 }
 
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, int QB = 1>
 hipError_t run_pp(FwdParams p, long long B, hipStream_t st) {
-  constexpr int BM = 256;
+  constexpr int BM = 256 * QB;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * p.Hq * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL>), dim3((int)nb), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL, QB>), dim3((int)nb), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
