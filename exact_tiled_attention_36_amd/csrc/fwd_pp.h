@@ -43,6 +43,9 @@
 #ifndef FWD_PP_LOOK
 #define FWD_PP_LOOK 4
 #endif
+#ifndef FWD_PP2_LOOK
+#define FWD_PP2_LOOK 3
+#endif
 
 namespace fa {
 namespace {
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
       // O += V_t P_t first: the weights die before the next scores are made
       if constexpr (PV) pv(Vb(t));
       if constexpr (NEXT) compute_s(Kb(t + 1));
-      ReadAheadG<FWD_PP_LOOK, NP, 2, NS, 2, QB>::emit();
+      ReadAheadG<FWD_PP2_LOOK, NP, 2, NS, 2, QB>::emit();
     }
     __builtin_amdgcn_sched_barrier(0);
   };

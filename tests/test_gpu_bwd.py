@@ -152,6 +152,43 @@ def test_bwd_stages_equal_whole(gpu_lib, shape):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+# d = 128 with at least 256 workgroups of 128 keys: the large-grid dK/dV kernel (one
+# 32-key slot per wave, 4 waves). Ragged query and key tails, both causal alignments
+# (Nq > Nk: the first rows see no key), GQA, MQA, non-causal and large logits; the GPU
+# computes every gradient, the oracle the first and the last (batch, kv-head) group.
+SHAPES_DKDV_LARGE = [
+    (1, 64, 16, 2100, 2100, 128, True, 1.0),
+    (2, 32, 32, 1000, 1300, 128, True, 1.0),    # Nk > Nq, key tail
+    (2, 32, 16, 1500, 1100, 128, True, 1.0),    # Nq > Nk: rows < 400 see no key
+    (1, 32, 32, 1100, 4200, 128, False, 1.0),
+    (4, 4, 1, 700, 9000, 128, True, 1.0),       # MQA, long keys
+    (1, 32, 32, 4100, 4100, 128, True, 4.0),    # large logits
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_DKDV_LARGE)
+def test_bwd_dkdv_large_grid_shapes(gpu_lib, shape):
+    import torch
+    B, Hq, Hkv, Nq, Nk, d, causal, qm = shape
+    assert -(-Nk // 128) * Hkv * B >= 256
+    inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, with_do=True, q_mult=qm,
+                            seed=3600 + Nq + 5 * Nk + Hkv)
+    what = f"dkdv-large{shape}"
+    announce(f"bwd {what}")
+    dq, dk, dv = gpu_fwd_bwd(gpu_lib, inp)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    g = Hq // Hkv
+    for (b, kvh) in ((0, 0), (B - 1, Hkv - 1)):
+        hs = slice(kvh * g, (kvh + 1) * g)
+        rq, rk, rv, _ = A.backward(inp.as_f64("q")[b:b + 1, hs], inp.as_f64("k")[b:b + 1, kvh:kvh + 1],
+                                   inp.as_f64("v")[b:b + 1, kvh:kvh + 1],
+                                   inp.as_f64("do")[b:b + 1, hs], inp.scale, causal)
+        assert_grad_close(to_host64(dq[b:b + 1, hs]), rq, f"{what} b{b} g{kvh} dQ")
+        assert_grad_close(to_host64(dk[b:b + 1, kvh:kvh + 1]), rk, f"{what} b{b} g{kvh} dK")
+        assert_grad_close(to_host64(dv[b:b + 1, kvh:kvh + 1]), rv, f"{what} b{b} g{kvh} dV")
+
+
 def test_c5_full_size_one_kv_group(gpu_lib):
     """The GQA training config at full size: the GPU computes every gradient; the
     oracle recomputes one (batch, kv-head) group in full (4 query heads, 8192 rows)."""
