@@ -90,6 +90,11 @@ SHAPES = [
     (1, 2, 2, 77, 333, 128, True),         # Nq < Nk: bottom-right diagonal
     (1, 2, 1, 300, 100, 128, True),        # Nq > Nk: first rows see no key
     (1, 3, 1, 130, 130, 256, True),
+    (2, 4, 2, 300, 300, 256, True),        # d = 256: GQA, ragged tail
+    (1, 2, 1, 200, 77, 256, False),        # d = 256: key tail
+    (1, 2, 2, 77, 333, 256, True),         # d = 256: bottom-right diagonal
+    (1, 2, 1, 300, 100, 256, True),        # d = 256: first rows see no key
+    (1, 8, 1, 129, 511, 256, True),        # d = 256: MQA
     (1, 8, 1, 129, 511, 64, True),         # MQA
     (2, 2, 2, 1, 700, 128, True),          # one query row
 ]
