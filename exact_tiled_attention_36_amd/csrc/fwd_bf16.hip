@@ -40,13 +40,20 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   // as its products, and the software-pipelined kernel below is 6-7 % faster.
   if (s.d == 256)
     return c ? run_pp<256, 32, true>(p, s.B, st) : run_pp<256, 32, false>(p, s.B, st);
-  // d = 128, long query sequences (4096 rows non-causal, 8192 causal): the two-group
-  // kernel with 64 rows per wave (fwd_pp.h, 512-row workgroups), when that still gives
-  // every compute unit a workgroup. Each K / V^T operand read from LDS then feeds two
-  // products. Time against the kernel below: B1 H8 N32768 causal -8 %, B2 Hq32 Hkv8
-  // N8192 causal -6.5 %, B2 H32 N4096 and B1 H8 N16384 non-causal -9 %; but B4 H32
-  // N4096 causal +1 %: there a 512-row workgroup walks the diagonal tiles for all of its
-  // rows, a larger share of the work.
+  // d = 128 from 4096 query rows: the two-group kernel with two 32-row query blocks per
+  // wave (fwd_pp.h), so each K / V^T operand read from LDS feeds two products, when it
+  // still gives every compute unit a workgroup.
+  //  - an even number of query heads per kv-head: the two blocks are the same rows of
+  //    two heads of one group (256-row workgroups). Time against the kernel below: B2
+  //    Hq32 Hkv8 N8192 causal -8 % (-3.7 % against 64 consecutive rows), B4 Hq32 Hkv8
+  //    N4096 causal -11 %.
+  //  - otherwise 64 consecutive rows of one head (512-row workgroups): B1 H8 N32768
+  //    causal -8 %, B2 H32 N4096 and B1 H8 N16384 non-causal -9 %, but B4 H32 N4096
+  //    causal +1 % (a 512-row workgroup walks the diagonal tiles for all of its rows, a
+  //    larger share of the work there), so causal from 8192 rows only.
+  const long long wghp = (long long)((s.Nq + 255) / 256) * (s.Hq / 2) * s.B;
+  if (s.d == 128 && (s.Hq / s.Hkv) % 2 == 0 && s.Nq >= kPp128MinRows && wghp >= kSmallGrid)
+    return c ? run_pp<128, 32, true, 2, true>(p, s.B, st) : run_pp<128, 32, false, 2, true>(p, s.B, st);
   const long long wg512 = (long long)((s.Nq + 511) / 512) * s.Hq * s.B;
   if (s.d == 128 && s.Nq >= (c ? 2 * kPp128MinRows : kPp128MinRows) && wg512 >= kSmallGrid)
     return c ? run_pp<128, 32, true, 2>(p, s.B, st) : run_pp<128, 32, false, 2>(p, s.B, st);

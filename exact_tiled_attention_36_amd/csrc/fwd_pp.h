@@ -54,12 +54,16 @@ namespace {
 // no special case (its weights are exp2(-inf) = 0, its first rescale factor 0)
 constexpr float kNoMax = -1e30f;
 
-template <int D, int BN, bool CAUSAL, int QB>
+template <int D, int BN, bool CAUSAL, int QB, bool HP = false>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   constexpr int NW = 8;
-  constexpr int RW = 32 * QB;    // query rows per wave (QB blocks of 32)
-  constexpr int BM = RW * NW;    // query rows per workgroup
+  static_assert(!HP || QB == 2, "head pairs take two query blocks");
+  // HP: the two blocks of a wave are the same 32 rows of two query heads that share a
+  // kv-head; otherwise QB consecutive 32-row blocks of one head
+  constexpr int RW = HP ? 32 : 32 * QB;  // query rows per wave
+  constexpr int BM = RW * NW;            // query rows per workgroup (per head)
+  constexpr int QSTEP = HP ? 0 : 32;     // row offset of block qb = QSTEP * qb
   constexpr int TILE = TL::elems(BN);
   constexpr int NKB = BN / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide chunks of d (reduction of S)
@@ -85,7 +89,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
     qb = L % p.nqb;
     bh = L / p.nqb;
   }
-  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int hpb = HP ? p.Hq / 2 : p.Hq;  // head slots per batch (pairs with HP)
+  const int h = HP ? 2 * (bh % hpb) : bh % hpb, b = bh / hpb;
   const int kvh = h / p.g;
   const int q0 = qb * BM;
   const int w0 = q0 + RW * wu;  // first query row of this wave
@@ -103,7 +108,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
     for (int dc = 0; dc < NDC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8_t, src[2 * dc]);
   }
   uint16_t* const q1t = smem + 4 * TILE + wu * QT;  // this wave's second Q block (QB = 2)
-  if constexpr (QB == 2) tile_load_async<D, 32, 1>(Qg, w0 + 32, p.Nq, q1t, 0, lane);
+  if constexpr (QB == 2)
+    tile_load_async<D, 32, 1>(HP ? Qg + (size_t)p.Nq * D : Qg, w0 + QSTEP, p.Nq, q1t, 0, lane);
   // nothing may be outstanding in the loop below except the tile copies it issues
   wait_vmem();
 
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         int last = p.Nk - 1;
-        if (CAUSAL) last = min(last, w0 + 32 * qb + l32 + p.causal_off);
+        if (CAUSAL) last = min(last, w0 + QSTEP * qb + l32 + p.causal_off);
         const int T = last - base;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -342,15 +348,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   // Epilogue: combine the two half-row sums, normalise once, store O and LSE.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = w0 + 32 * qb + l32;
+    const int qrow = w0 + QSTEP * qb + l32;
+    const int hq = HP ? h + qb : h;
     const float ltot = xhalf_sum(lsum[qb]);
     if (qrow < p.Nq) {
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       if (hi == 0) {
-        p.lse[(size_t)(b * p.Hq + h) * p.Nq + qrow] =
+        p.lse[(size_t)(b * p.Hq + hq) * p.Nq + qrow] =
             ltot > 0.f ? (m[qb] + log2f(ltot)) * kLn2 : -INFINITY;
       }
-      uint16_t* orow = p.o + ((size_t)(b * p.Hq + h) * p.Nq + qrow) * D;
+      uint16_t* orow = p.o + ((size_t)(b * p.Hq + hq) * p.Nq + qrow) * D;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -364,13 +371,13 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BN, bool CAUSAL, int QB = 1>
+template <int D, int BN, bool CAUSAL, int QB = 1, bool HP = false>
 hipError_t run_pp(FwdParams p, long long B, hipStream_t st) {
-  constexpr int BM = 256 * QB;
+  constexpr int BM = HP ? 256 : 256 * QB;
   p.nqb = (p.Nq + BM - 1) / BM;
-  const long long nb = (long long)p.nqb * p.Hq * B;
+  const long long nb = (long long)p.nqb * (HP ? p.Hq / 2 : p.Hq) * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL, QB>), dim3((int)nb), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL, QB, HP>), dim3((int)nb), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

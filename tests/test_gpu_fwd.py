@@ -85,25 +85,34 @@ def test_large_grid_shapes_bf16(gpu_lib, shape):
     check_full(gpu_lib, inp, f"large{shape}")
 
 
-# d = 128 from 4096 query rows non-causal, 8192 causal (with at least 256 workgroups
-# of 512 rows) runs the two-group kernel with 64 rows per wave. Ragged query and key tails, both causal
-# alignments (Nq > Nk leaves the first rows with no visible key: O = 0, lse = -inf),
-# GQA, non-causal and large logits; whole heads compared with the oracle (the first,
-# a middle and the last head: the first and last XCD's shares).
+# d = 128 from 4096 query rows (with at least 256 workgroups) runs the two-group kernel
+# with two 32-row query blocks per wave: the same rows of two query heads of one group
+# when a kv-head has an even number of query heads ("pairs"), else 64 consecutive rows
+# of one head (causal from 8192 rows). Ragged query and key tails, both causal alignments
+# (Nq > Nk leaves the first rows with no visible key: O = 0, lse = -inf), GQA/MQA,
+# non-causal and large logits; whole heads compared with the oracle (the first, a
+# middle and the last head: the first and last XCD's shares).
 PP128 = [
-    (1, 32, 8, 8200, 8200, 128, True, 1.0),
-    (1, 32, 32, 8192, 8600, 128, True, 1.0),   # Nk > Nq, key tail of 24
-    (1, 64, 8, 4500, 3000, 128, False, 1.0),   # non-causal, Nq > Nk
-    (1, 32, 32, 9000, 8000, 128, True, 1.0),   # Nq > Nk: rows < 1000 see no key
-    (1, 32, 16, 8193, 8193, 128, True, 4.0),   # large logits, one-row tail block
-    (1, 64, 64, 4097, 4097, 128, False, 4.0),
+    (1, 32, 8, 8200, 8200, 128, True, 1.0),    # pairs
+    (1, 32, 32, 8192, 8600, 128, True, 1.0),   # rows; Nk > Nq, key tail of 24
+    (1, 64, 8, 4500, 3000, 128, False, 1.0),   # pairs; non-causal, Nq > Nk
+    (1, 32, 32, 9000, 8000, 128, True, 1.0),   # rows; Nq > Nk: rows < 1000 see no key
+    (1, 32, 16, 8193, 8193, 128, True, 4.0),   # pairs; large logits, one-row tail block
+    (1, 64, 64, 4097, 4097, 128, False, 4.0),  # rows
+    (1, 32, 8, 4100, 4100, 128, True, 1.0),    # pairs, causal from 4096 rows
+    (1, 32, 16, 5000, 4000, 128, True, 1.0),   # pairs; Nq > Nk
+    (2, 16, 8, 4096, 4500, 128, True, 1.0),    # pairs; Nk > Nq, two batches
+    (1, 64, 1, 4100, 4100, 128, True, 1.0),    # MQA (64 heads per kv-head): pairs
 ]
 
 
 @pytest.mark.parametrize("shape", PP128)
 def test_pp128_shapes_bf16(gpu_lib, shape):
     B, Hq, Hkv, Nq, Nk, d, causal, qm = shape
-    assert Nq >= (8192 if causal else 4096) and -(-Nq // 512) * Hq * B >= 256
+    if (Hq // Hkv) % 2 == 0:
+        assert Nq >= 4096 and -(-Nq // 256) * (Hq // 2) * B >= 256
+    else:
+        assert Nq >= (8192 if causal else 4096) and -(-Nq // 512) * Hq * B >= 256
     inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, q_mult=qm,
                             seed=2500 + Nq + Nk + Hkv)
     what = f"pp128{shape}"
@@ -111,10 +120,10 @@ def test_pp128_shapes_bf16(gpu_lib, shape):
     o, lse = run_fwd(gpu_lib, inp)
     assert np.all(np.isfinite(o))
     qf, kf, vf = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
-    for h in (0, Hq // 2 + 1, Hq - 1):
-        o_ref, lse_ref = A.forward_head(qf, kf, vf, inp.scale, inp.causal, 0, h)
-        assert_o_close(o[0, h], o_ref, f"{what} h{h}")
-        assert_lse_close(lse[0, h], lse_ref, TOL_LSE_BF16, f"{what} h{h}")
+    for b, h in ((0, 0), (0, Hq // 2 + 1), (B - 1, Hq - 1)):
+        o_ref, lse_ref = A.forward_head(qf, kf, vf, inp.scale, inp.causal, b, h)
+        assert_o_close(o[b, h], o_ref, f"{what} b{b} h{h}")
+        assert_lse_close(lse[b, h], lse_ref, TOL_LSE_BF16, f"{what} b{b} h{h}")
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 1, 70, 90, 4, True), (1, 1, 1, 33, 33, 20, False),
