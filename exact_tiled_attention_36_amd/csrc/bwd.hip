@@ -17,7 +17,9 @@
 //     scalars, and dQ^T += K^T dS^T reads K^T with LDS transpose loads. Its prologue
 //     forms D_i from its rows of O and dO (dO is in registers already) and stores D
 //     and LSE * log2(e) for the second kernel.
-//  2. bwd_dkdv (bwd_dkdv.h): one workgroup per (batch, kv-head, 128 keys); each wave
+//  2. bwd_dkdv (bwd_dkdv.h; bwd_dkdv_rs.h at d = 256, 64 keys per workgroup, the
+//     products of each 32 keys split between two waves): one workgroup per (batch,
+//     kv-head, 128 keys); each wave
 //     keeps 32 keys of K and V in registers and loops over the group's query heads and
 //     the query blocks that can see its keys (diagonal blocks first, then the unmasked
 //     ones block by block from the last down, all heads of the group per block, so the
@@ -29,6 +31,7 @@
 // No atomics: every output element is written by exactly one workgroup, so results
 // are bitwise reproducible.
 #include "bwd_dq.h"
+#include "bwd_dkdv_rs.h"
 
 namespace fa {
 namespace {
@@ -55,7 +58,7 @@ hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
     // (d = 64, 128).
     const long long wg128 = (long long)((p.Nk + 127) / 128) * p.Hkv * B;
     const bool split = BMQ == 64 && wg128 < 256;
-    const int bnk = split ? 64 : 128;
+    const int bnk = split || D == 256 ? 64 : 128;
     const int nkb = (p.Nk + bnk - 1) / bnk;
     const long long n = (long long)nkb * p.Hkv * B;
     if (n > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -69,7 +72,8 @@ hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, BMQ, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nkb);
       e = hipGetLastError();
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, BMQ, CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nkb);
+      static_assert(D == 256, "32-query tiles are the d = 256 form");
+      hipLaunchKernelGGL((bwd_dkdv_rs_kernel<CAUSAL>), dim3((int)n), dim3(256), 0, st, p, nkb);
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

@@ -81,6 +81,11 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm("" : "+v"(x));
   return x;
 }
+// The same for a wave-uniform value kept in a scalar register.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
+  asm("" : "+s"(x));
+  return x;
+}
 // Marks x as needed here: volatile asm is never moved, so the computation of x cannot
 // be sunk past this point (e.g. across a barrier into the next loop iteration).
 __device__ __forceinline__ void pin(uint32_t x) { asm volatile("" ::"v"(x)); }
