@@ -122,36 +122,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_rs_kernel(BwdParams p, int nk
   auto qtile = [&](int s) FA_INLINE { return smem + (s % NB) * 2 * TILE; };
   auto stats = [&](int s) FA_INLINE { return svec + (s % NB) * 2 * SV; };
   const uint32_t lane_off = 4u * lane;
-  // Copy of one 32-row tile (rows i0.. of G) to the LDS tile at byte address m0t, in
-  // 256-byte pieces (half rows): wave wu takes half (wu & 1) of rows wu/2 + 2i. The
-  // LDS address of each piece is m0t plus constants; m0t passes through opaque_s() so
-  // that the compiler adds them in the loop instead of keeping one scalar register per
-  // piece and buffer. A tile reaching past Nq re-reads the last row for the rows
-  // beyond it, one scalar base per piece.
-  using PC = PieceCopy<BfRows<D>, BMQ, NW>;
-  auto copy_tile = [&](const uint16_t* G, int i0, uint32_t m0t, bool ragged) FA_INLINE {
-    const uint32_t m0w = opaque_s(m0t + (uint32_t)BfRows<D>::piece_bytes(wu));
-    if (!ragged) {
-      PC::all((const char*)(G + (size_t)i0 * D) + 256 * wu, lane_off, m0w,
-              std::make_integer_sequence<int, PC::NI>());
-    } else {
-#pragma unroll
-      for (int i = 0; i < PC::NI; ++i) {
-        const int r = min(i0 + (wu >> 1) + 2 * i, p.Nq - 1);
-        lds_dma_row_imm<0>(G + (size_t)r * D + 128 * (wu & 1), lane_off,
-                           m0w + (uint32_t)PC::lds_off(0, i));
-      }
-    }
-  };
-  // copies of the tiles of step s (Q, dO) and of their LSE2 (wave 0) and D (wave 1)
-  // rows, spread over the 4 waves
+  // copies of the tiles of step s (Q, dO; rows past Nq re-read the last row) and of
+  // their LSE2 (wave 0) and D (wave 1) rows, spread over the 4 waves
   auto issue = [&](int s, const Cur& c) FA_INLINE {
     const size_t hbase = (size_t)(b * p.Hq + kvh * p.g + c.hs) * p.Nq;
     const int i0 = cur_i0(c);
-    const bool ragged = i0 + BMQ > p.Nq;
     const uint32_t m0t = lds_addr(qtile(s));
-    copy_tile(p.q + hbase * D, i0, m0t, ragged);
-    copy_tile(p.dO + hbase * D, i0, m0t + 2 * TILE, ragged);
+    tile_load_m0<D, BMQ, NW>(p.q + hbase * D, i0, p.Nq, m0t, wu, lane_off);
+    tile_load_m0<D, BMQ, NW>(p.dO + hbase * D, i0, p.Nq, m0t + 2 * TILE, wu, lane_off);
     if (wu < 2) vec_load_async((wu ? p.dvec : p.lse2v) + hbase, i0, p.Nq - 1, stats(s) + wu * SV, lane);
   };
 

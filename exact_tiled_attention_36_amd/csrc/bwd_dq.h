@@ -117,6 +117,12 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
   const uint32_t lane_off = 4u * lane;
   auto load_tile = [&](int t) FA_INLINE {
+    if constexpr (D == 256) {
+      const uint32_t m0 = lds_addr(Kb(t));
+      tile_load_m0<D, BN, NW>(Kg, t * BN, p.Nk, m0, wu, lane_off);
+      tile_load_m0<D, BN, NW>(Vg, t * BN, p.Nk, m0 + 2 * TILE, wu, lane_off);
+      return;
+    }
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
         tile_load_full<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);

@@ -359,6 +359,33 @@ __device__ __forceinline__ void tile_load_full(const uint16_t* G, int j0, uint16
   PieceCopy<BfRows<D>, ROWS, NW>::run(G + (size_t)j0 * D, lds, wu, lane_off);
 }
 
+// The same copy (d = 128 or 256) for kernels that keep many scalar values live: the LDS
+// address of each piece is formed in the loop from one scalar base that passes through
+// opaque_s(), so the compiler does not keep one scalar register per piece and buffer
+// (which spills to vector lanes and costs a read per piece). lds_m0: LDS byte address
+// of the tile. A tile that reaches past nrows re-reads row nrows-1 for the rows beyond,
+// with one scalar base per piece.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_load_m0(const uint16_t* G, int j0, int nrows,
+                                             uint32_t lds_m0, int wu, uint32_t lane_off) {
+  static_assert(D == 128 || D == 256, "pieces of whole or half rows");
+  using PC = PieceCopy<BfRows<D>, ROWS, NW>;
+  constexpr int PPR = D / 128;  // pieces per row
+  static_assert(NW % PPR == 0, "a wave's pieces share their column half");
+  const uint32_t m0w = opaque_s(lds_m0 + (uint32_t)BfRows<D>::piece_bytes(wu));
+  if (j0 + ROWS <= nrows) {
+    PC::all((const char*)(G + (size_t)j0 * D) + 256 * wu, lane_off, m0w,
+            std::make_integer_sequence<int, PC::NI>());
+  } else {
+#pragma unroll
+    for (int i = 0; i < PC::NI; ++i) {
+      const int r = min(j0 + wu / PPR + (NW / PPR) * i, nrows - 1);
+      lds_dma_row_imm<0>(G + (size_t)r * D + 128 * (wu % PPR), lane_off,
+                         m0w + (uint32_t)PC::lds_off(0, i));
+    }
+  }
+}
+
 // Scheduling hint for a run of N1 operand groups of R1 LDS reads followed by N2 groups
 // of R2 reads, each group feeding QB consecutive products: the reads are issued LOOK
 // ahead of the products that use them (sched_group_barrier groups, in program order).
