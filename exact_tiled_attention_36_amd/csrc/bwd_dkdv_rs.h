@@ -140,6 +140,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_rs_kernel(BwdParams p, int nk
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   static_assert(TL::shifts_ok(BMQ), "LDS reads add row offsets as constants");
 
+  // dV/dK operands of the second 16 queries of the previous step, carried into the
+  // next one (zero before the first step)
+  bf16x8_t gcar[NCB], pcar;
+  {
+    const u32x4_t z = {0, 0, 0, 0};
+    pcar = __builtin_bit_cast(bf16x8_t, z);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) gcar[cb] = pcar;
+  }
+
   // One step: the 32-query slice of one tile. MASK: the weight wave masks (causal
   // diagonal, rows past Nq); the dS wave needs no mask (masked weights are 0).
   auto step = [&](auto role_tag, auto mask_tag, int s, int i0) FA_INLINE {
@@ -226,12 +236,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_rs_kernel(BwdParams p, int nk
     using IHD = std::integral_constant<int, HD>;
     using INCB = std::integral_constant<int, NCB>;
 
-    // S/dP over the two halves of d, then the vector work of the first 16 queries,
-    // dV/dK of those beside the vector work of the other 16, then theirs
+    // The row reads of this step beside dV/dK of the previous step's second 16 queries
+    // (registers only), then S/dP over the two halves of d, the vector work of the
+    // first 16 queries, and dV/dK of those beside the vector work of the other 16.
+    // The products of those 16 go to the next step (or to the end of the loop).
     rd_row(0, NDC);
     rd_st();
-    __builtin_amdgcn_sched_barrier(0);
     debug_sync();
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma32x32x16(gcar[cb], pcar, acc[cb]);
+    interleave(INCB());
     mm_x(0, HD);
     rd_g(0, 0);
     interleave(IHD());
@@ -245,9 +259,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_rs_kernel(BwdParams p, int nk
     vec(1);
     interleave(INCB());
     pin(pc[1]);
-    mm_g(1, 1);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) gcar[cb] = ga[1][cb];
+    pcar = pc[1];
     debug_sync();
+  };
+  // the carried products of the last step
+  auto flush = [&]() FA_INLINE {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma32x32x16(gcar[cb], pcar, acc[cb]);
   };
 
   Cur cur = {0, 0, 0};
@@ -280,6 +300,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_rs_kernel(BwdParams p, int nk
       wait_vmem();
       __syncthreads();
     }
+    flush();
     if (total > 0) {  // the dS waves' last step
       debug_sync();
       debug_sync();
@@ -303,6 +324,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_rs_kernel(BwdParams p, int nk
       wait_vmem();
       __syncthreads();
     }
+    flush();
   }
 
   if (key < p.Nk) {
