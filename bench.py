@@ -265,10 +265,35 @@ def extras(torch, fa, iters=50):
         out[name] = rec
         del q, k, v, o, lse
         torch.cuda.empty_cache()
+    out["c3b_bf16_causal_B2H16N4096d256_backward"] = backward_d256(torch, fa, g, iters)
     out["c2_bf16_B2H16N1024d64_rotated"] = rotated_small(torch, fa, g)
     out["decode_gqa_B16Hq32Hkv4Nq1Nk8192d128"] = gqa_decode(torch, fa, g, iters)
     out["v1_vs_v2"] = version_ablation(torch, fa, g)
     out["fp8_forward"] = fp8_forward(torch, fa, g, out)
+    return out
+
+
+def backward_d256(torch, fa, g, iters):
+    """Recompute backward at B2 H16 N4096 d256 causal: dQ with D (stage 0), dK/dV
+    (stage 1, the split-slot kernel) and both, after one forward for O and LSE. Flops:
+    dQ three products, dK/dV four, of the forward's two."""
+    B, H, N, d = 2, 16, 4096, 256
+    rnd = lambda: torch.randn(B, H, N, d, device="cuda", dtype=torch.bfloat16, generator=g)
+    q, k, v, do = rnd(), rnd(), rnd(), rnd()
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device="cuda", dtype=torch.float32)
+    fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, H, N, N, d), device="cuda", dtype=torch.uint8)
+    f = fwd_flops(B, H, N, N, d, True)
+    out = {}
+    for stage, name, mult in ((0, "dq_kernel", 1.5), (1, "dkdv_kernel", 2.0), (-1, "whole", 2.5)):
+        call = lambda stage=stage: fa.bwd(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv,
+                                          workspace=ws, stage=stage)
+        out[name] = with_stats({}, timed_stats(torch, call, iters), mult * f)
+    out["kernels"] = "bwd_dq_kernel<256, 32, 4, true>, bwd_dkdv_rs_kernel<true>"
+    del q, k, v, do, o, dq, dk, dv, ws
+    torch.cuda.empty_cache()
     return out
 
 
@@ -396,7 +421,8 @@ def profile_tail(torch, fa, calls=3):
     cores busy by construction: the reference for the busy-cycle counter), the
     non-causal B2 H16 N1024 d64 forward, split-KV decode at B8 H8 Nk32768 d128 (one row
     per kv-head) and B16 Hq32 Hkv4 Nk8192 d128 (eight rows), and the causal forward at
-    B4 H32 N4096 d128, B2 H16 N4096 d256 and B1 H8 N32768 d128."""
+    B4 H32 N4096 d128, B2 H16 N4096 d256 and B1 H8 N32768 d128, and the d256 backward
+    (B2 H16 N4096 causal)."""
     g = torch.Generator(device="cuda")
     g.manual_seed(99)
     out = torch.empty(1024 * 256, device="cuda", dtype=torch.float32)
@@ -419,6 +445,18 @@ def profile_tail(torch, fa, calls=3):
         for _ in range(2):
             fa.fwd(q, k, v, causal=True)
         del q, k, v
+    # the d = 256 backward at B2 H16 N4096 causal: dQ with D, then dK/dV, twice
+    q, k, v, do = (rnd(2, 16, 4096, 256) for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 16, 4096, device="cuda", dtype=torch.float32)
+    fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(2, 16, 16, 4096, 4096, 256), device="cuda",
+                     dtype=torch.uint8)
+    for _ in range(2):
+        for stage in (0, 1):
+            fa.bwd(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws,
+                   stage=stage)
     torch.cuda.synchronize()
 
 
