@@ -193,8 +193,7 @@ struct TileLayout {
 // latency of a prefetch that targets a different buffer. Completion is therefore
 // the caller's business: wait_vmem() and a workgroup barrier before the buffer is
 // read. M0 holds the LDS base; one wait state separates its write from the load.
-__device__ __forceinline__ void lds_dma_dword(const void* src, const void* lds_base) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)(const FA_LDS void*)lds_base;
+__device__ __forceinline__ void lds_dma_dword_m0(const void* src, uint32_t m0v) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
@@ -202,6 +201,9 @@ __device__ __forceinline__ void lds_dma_dword(const void* src, const void* lds_b
       :
       : "v"(src), "s"(m0v)
       : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_dword(const void* src, const void* lds_base) {
+  lds_dma_dword_m0(src, (uint32_t)(uintptr_t)(const FA_LDS void*)lds_base);
 }
 
 // Same copy with a wave-uniform global base and a per-lane byte offset (the saddr
