@@ -360,6 +360,16 @@ __device__ __forceinline__ void tile_load_full(const uint16_t* G, int j0, uint16
                                                uint32_t lane_off) {
   PieceCopy<BfRows<D>, ROWS, NW>::run(G + (size_t)j0 * D, lds, wu, lane_off);
 }
+// The same, with the wave's first LDS address passed through opaque_s() (see
+// tile_load_m0): for kernels where the hoisted per-piece addresses spill.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_load_full_o(const uint16_t* G, int j0, uint16_t* lds, int wu,
+                                                 uint32_t lane_off) {
+  using PC = PieceCopy<BfRows<D>, ROWS, NW>;
+  const uint32_t m0w = opaque_s(lds_addr(lds) + (uint32_t)BfRows<D>::piece_bytes(wu));
+  PC::all((const char*)(G + (size_t)j0 * D) + 256 * wu, lane_off, m0w,
+          std::make_integer_sequence<int, PC::NI>());
+}
 
 // The same copy (d = 128 or 256) for kernels that keep many scalar values live: the LDS
 // address of each piece is formed in the loop from one scalar base that passes through

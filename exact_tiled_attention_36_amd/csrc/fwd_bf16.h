@@ -164,7 +164,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   auto load = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
-        tile_load_full<D, BN, NW>(G, t * BN, dst, wu, lane_off);
+        // the 4-wave and non-causal kernels keep too many scalar values for the
+        // per-piece LDS addresses the compiler would hoist (they spilled into vector
+        // lanes: small-grid d = 128 forward 10 % faster without); the causal 8-wave
+        // kernels did not spill and keep the hoisted form (1-3 % faster there)
+        if constexpr (CAUSAL && NW == 8)
+          tile_load_full<D, BN, NW>(G, t * BN, dst, wu, lane_off);
+        else
+          tile_load_full_o<D, BN, NW>(G, t * BN, dst, wu, lane_off);
         return;
       }
     }
