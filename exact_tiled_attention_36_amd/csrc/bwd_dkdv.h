@@ -193,7 +193,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     sp.i0 = cur_i0(c);
     return sp;
   };
-  auto dma_piece = [&](int s, const StepPos& ps, int j) FA_INLINE {
+  // D = 128: the LDS address of row wu + 4i is that of row wu plus a constant (checked
+  // below); the base passes through opaque_s() once per step (m0q), so the compiler
+  // does not keep one scalar register per row and buffer (they spilled into vector
+  // lanes in the split form)
+  constexpr auto wave_independent = []() {
+    for (int w = 0; w < 4; ++w)
+      for (int i = 0; i < PPW; ++i)
+        if (TL::row(w + 4 * i) - TL::row(w) != TL::row(4 * i) - TL::row(0)) return false;
+    return true;
+  };
+  static_assert(D != 128 || wave_independent(), "row offsets of a wave's pieces depend on the wave");
+  auto dma_piece = [&](int s, const StepPos& ps, int j, uint32_t m0q) FA_INLINE {
     const uint16_t* G = j < PPW ? ps.q : ps.dO;
     uint16_t* tile = qtile(s) + (j < PPW ? 0 : TILE);
     const int k = wu + 4 * (j % PPW);  // piece of the tile (uniform)
@@ -203,9 +214,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
       lds_dma_dword(G + (size_t)min(ps.i0 + r, p.Nq - 1) * D + 2 * (lane & 31),
                     tile + TL::row(2 * k));
     } else {
-      constexpr int PPR = D / 128;  // pieces per row
-      const int r = k / PPR, c0 = (k % PPR) * 128;
-      lds_dma_row(G + (size_t)min(ps.i0 + r, p.Nq - 1) * D + c0, lane_off, tile + TL::row(r) + c0);
+      static_assert(D == 128, "one piece per row");
+      const int jj = j % PPW;
+      const uint32_t m0 = m0q + (j < PPW ? 0u : 2u * TILE) + 2u * (TL::row(4 * jj) - TL::row(0));
+      lds_dma_row_imm<0>(G + (size_t)min(ps.i0 + k, p.Nq - 1) * D, lane_off, m0);
     }
   };
   // LSE2 rows by waves 0 and 2, D rows by waves 1 and 3 (identical duplicate copies
@@ -217,8 +229,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
     for (int c = 0; c < SV / 64; ++c) vec_load_async(src, ps.i0 + 64 * c, p.Nq - 1, sv + 64 * c, lane);
   };
   auto issue_at = [&](int s, const StepPos& ps) FA_INLINE {
+    const uint32_t m0q = D == 128 ? opaque_s(lds_addr(qtile(s)) + 2u * TL::row(wu)) : 0u;
 #pragma unroll
-    for (int j = 0; j < 2 * PPW; ++j) dma_piece(s, ps, j);
+    for (int j = 0; j < 2 * PPW; ++j) dma_piece(s, ps, j, m0q);
     dma_stats(s, ps);
   };
   // Copies of a tile whose rows all lie below Nq, for D = 128: wave w copies rows
@@ -235,7 +248,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p, int nkb) 
                  vo2 = lane_off + 1024u - 544u, vo3 = lane_off + 1024u - 816u;
   auto issue_full = [&](int s, const StepPos& ps) FA_INLINE {
     if constexpr (D == 128 && BMQ == 64) {
-      const uint32_t qb = (uint32_t)(uintptr_t)(const FA_LDS void*)qtile(s) + 320u * wu;
+      // (the split form passes the base through opaque_s(): its hoisted per-buffer
+      // addresses spilled into vector lanes)
+      const uint32_t qb0 = (uint32_t)(uintptr_t)(const FA_LDS void*)qtile(s) + 320u * wu;
+      const uint32_t qb = SPLIT ? opaque_s(qb0) : qb0;
       const char* gq = (const char*)(ps.q + (size_t)(ps.i0 + wu) * D) - 1024;
       const char* go = (const char*)(ps.dO + (size_t)(ps.i0 + wu) * D) - 1024;
 #pragma unroll

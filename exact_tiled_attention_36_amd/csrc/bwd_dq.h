@@ -125,8 +125,15 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
     }
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
-        tile_load_full<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
-        tile_load_full<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
+        // (4-wave kernels: from one opaque LDS base, as their hoisted per-piece
+        // addresses spilled into vector lanes; the 8-wave ones were 1 % faster hoisted)
+        if constexpr (NW == 4) {
+          tile_load_full_o<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
+          tile_load_full_o<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
+        } else {
+          tile_load_full<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
+          tile_load_full<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
+        }
         return;
       }
     }
