@@ -13,10 +13,12 @@
 //                    (masked, bf16), dV += dO^T P; it hands P to its partner in LDS;
 //   the dS wave:     V in registers; dP = dO V^T, dS = P * (dP - D) with the
 //                    partner's P, dK += Q^T dS, one step behind.
-// Each wave holds 64 operand and 128 accumulator registers, about 360 in all: no
-// scratch. Q/dO tiles and their LSE2/D rows are triple buffered (step s: the weight
+// Each wave holds 64 operand (K or V) and 128 accumulator registers, about 320 in all:
+// no scratch. Q/dO tiles and their LSE2/D rows are triple buffered (step s: the weight
 // waves read tile s, the dS waves tile s-1, the copies of tile s+1 land in the third
 // buffer), the exchanged weights double buffered; one barrier per step orders it all.
+// The last eight products of a step (dV/dK of its second 16 queries, registers only)
+// run after the barrier, beside the next step's row reads.
 //
 // The dS wave multiplies dP - D by the bf16 weight the dV product uses too (the
 // one-wave kernel uses the float32 weight): the results differ within one bf16
