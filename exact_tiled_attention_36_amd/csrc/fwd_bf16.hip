@@ -1,7 +1,8 @@
 // Forward attention, bf16: launches of the software-pipelined kernel in fwd_bf16.h
 // (d = 64, and d = 128 for shorter sequences: 8-wave workgroups) and of the two-group
 // kernel in fwd_pp.h (d = 256, and d = 128 for long sequences), and the first-version
-// comparison forms; small grids go to fwd_bf16_small.hip.
+// comparison forms; small grids and short key ranges (d = 64, and causal d = 128) go
+// to the 4-wave kernels of fwd_bf16_small.hip.
 #include "fwd_bf16.h"
 #include "fwd_pp.h"
 
@@ -16,6 +17,7 @@ constexpr long long kSmallGrid = FWD_SMALL_GRID;
 #define FWD_PP128_MIN_ROWS 4096
 #endif
 constexpr int kPp128MinRows = FWD_PP128_MIN_ROWS;
+constexpr int kSmallKeys64 = 4096, kSmallKeys128 = 2048;
 
 }  // namespace
 
@@ -57,6 +59,14 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   const long long wg512 = (long long)((s.Nq + 511) / 512) * s.Hq * s.B;
   if (s.d == 128 && s.Nq >= (c ? 2 * kPp128MinRows : kPp128MinRows) && wg512 >= kSmallGrid)
     return c ? run_pp<128, 32, true, 2>(p, s.B, st) : run_pp<128, 32, false, 2>(p, s.B, st);
+  // For short key ranges the 4-wave kernel is also the faster one on large grids: two
+  // of its 128-row workgroups share a compute unit (80 KB of LDS and 252 registers per
+  // wave each), so one's start and end overlap the other's key loop. Measured against
+  // the 8-wave kernel (B4 H32): d64 causal N2048 -11 %, N4096 -4 to -6 %, d64
+  // non-causal N4096 -3.5 %, d128 causal N2048 -5 %; but d128 causal N4096 +0-2 %, d128
+  // non-causal N4096 +14 %, N6144 d128 and N8192 d64 causal +2-3 %.
+  if ((s.d == 64 && s.Nk <= kSmallKeys64) || (s.d == 128 && c && s.Nk <= kSmallKeys128))
+    return launch_fwd_bf16_small(p, s.B, s.d, c, st);
   switch (s.d) {
 #ifndef FWD_CFG128
 #define FWD_CFG128 64, 8, 1

@@ -63,17 +63,23 @@ def test_edge_shapes_bf16(gpu_lib, shape):
     check_full(gpu_lib, inp, f"edge{shape}")
 
 
-# Grids of at least 256 workgroups of 256 query rows run the 8-wave kernel; the shapes
-# above are small enough to take the 4-wave (128-row) one. These give the 8-wave
-# kernel ragged key tails, GQA and both causal alignments, compared element by element.
+# Grids of at least 256 workgroups of 256 query rows: the 4-wave (128-row) kernel up to
+# 4096 keys at d = 64 and up to 2048 keys for causal d = 128 (two of its workgroups per
+# compute unit), else the 8-wave kernel (below the two-group kernel's range); the
+# shapes above are small grids, which take the 4-wave kernel too. Ragged key tails, GQA
+# and both causal alignments, compared element by element.
 LARGE_GRID = [
-    (2, 32, 8, 1000, 1000, 128, True),
-    (2, 32, 4, 1000, 1300, 64, True),       # Nk > Nq: bottom-right diagonal
-    (2, 32, 32, 1100, 700, 128, False),     # Nq > Nk, non-causal
+    (2, 32, 8, 1000, 1000, 128, True),      # 4-wave
+    (2, 32, 4, 1000, 1300, 64, True),       # 4-wave; Nk > Nq: bottom-right diagonal
+    (2, 32, 32, 1100, 700, 128, False),     # 8-wave; Nq > Nk, non-causal
     # causal row-block orders: 72 (batch, head) pairs = 9 per XCD (pairs of heads and
     # one head alone); 68 pairs do not split evenly over 8 XCDs (level-major order)
-    (3, 24, 8, 1000, 1000, 128, True),
-    (1, 68, 17, 1000, 1000, 64, True),
+    (3, 24, 8, 1000, 1000, 128, True),      # 4-wave
+    (1, 68, 17, 1000, 1000, 64, True),      # 4-wave
+    (1, 24, 24, 4200, 4300, 128, True),     # 8-wave; Nk > Nq, key tail
+    (1, 32, 32, 3000, 2500, 128, True),     # 8-wave; Nq > Nk
+    (1, 17, 17, 4400, 4400, 64, True),      # 8-wave; 17 heads: level-major order
+    (1, 16, 4, 4500, 4100, 64, False),      # 8-wave; d = 64 non-causal, Nq > Nk
 ]
 
 
