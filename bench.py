@@ -44,7 +44,7 @@ WORKLOAD = "c5_bf16_causal_gqa_B2Hq32Hkv8N8192d128"
 KERNEL_SOURCES = {
     "fwd_pp_kernel": ["fwd_pp.h", "fwd_bf16.h", "fwd_bf16.hip", "common.h"],
     "bwd_dkdv_kernel": ["bwd_dkdv.h", "bwd_dkdv_d128.hip", "bwd.hip", "common.h"],
-    "bwd_dq_kernel": ["bwd_dq.h", "bwd.hip", "bwd_dkdv.h", "common.h"],
+    "bwd_dq_kernel": ["bwd_dq.h", "bwd_dq_small.hip", "bwd.hip", "bwd_dkdv.h", "common.h"],
 }
 
 

@@ -30,11 +30,11 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
-# Options for single files: the d = 128 dK/dV kernel and the small-grid forward and dQ kernels
-# have their matrix products write ordinary vector registers (see the files' headers). The
-# d = 128 dK/dV kernel is scheduled by the compiler's max-ILP strategy (0.6-2 % faster than
-# the default, no scratch), the other backward kernels by its iterative-ILP strategy (the
-# 8-wave dQ kernel 1-4 % faster, no kernel in that file spills more).
+# Options for single files: the d = 128 dK/dV kernel and the 4-wave forward and d = 64/128
+# dQ kernels have their matrix products write ordinary vector registers (see the files'
+# headers). The d = 128 dK/dV kernel is scheduled by the compiler's max-ILP strategy (0.6-2 %
+# faster than the default, no scratch), the rest of the backward (bwd.hip: d = 64 and 256
+# dK/dV, d = 256 dQ) by its iterative-ILP strategy (no kernel in that file spills more).
 FILE_FLAGS = {"bwd_dkdv_d128.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form",
                                     "-mllvm", "--amdgpu-sched-strategy=max-ilp"],
               "fwd_bf16_small.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],

@@ -11,8 +11,8 @@
 // with dK, dV summed over the query heads that share a key/value head.
 //
 // Two kernels on one stream:
-//  1. bwd_dq (bwd_dq.h; first): one workgroup per (batch, head, 32 queries per wave: 256 at
-//     d <= 128, 128 at d = 256); Q and dO stay in registers, K/V tiles are triple
+//  1. bwd_dq (bwd_dq.h; first): one workgroup per (batch, head, 128 queries: 4 waves of
+//     32; d = 64 and 128 from bwd_dq_small.hip); Q and dO stay in registers, K/V tiles are triple
 //     buffered in LDS; S^T and dP^T put one query per lane, so LSE and D are per-lane
 //     scalars, and dQ^T += K^T dS^T reads K^T with LDS transpose loads. Its prologue
 //     forms D_i from its rows of O and dO (dO is in registers already) and stores D
@@ -96,16 +96,14 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.scale = s.scale;
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
-  // dQ grids too small for one 256-row workgroup per compute unit use 128-row ones (4
-  // waves): twice the workgroups, no compute unit left idle (dK/dV is unchanged)
-  const long long dq256 = (long long)((s.Nq + 255) / 256) * s.Hq * s.B;
-  if (dq256 < 256 && (s.d == 64 || s.d == 128)) {
-    if (s.d == 64) return c ? run<64, 64, 32, 4, true>(p, s.B, stage, st) : run<64, 64, 32, 4, false>(p, s.B, stage, st);
-    return c ? run<128, 64, 32, 4, true>(p, s.B, stage, st) : run<128, 64, 32, 4, false>(p, s.B, stage, st);
-  }
+  // dQ runs in 128-row workgroups of 4 waves at every head size: two of them share a
+  // compute unit (61 KB of LDS and 254 registers per wave at d = 128), so one's start
+  // and end overlap the other's key loop. Measured against 256-row workgroups of 8
+  // waves: B2 Hq32 Hkv8 N8192 d128 causal -1.5 %, B4 H32 N4096 d128 causal -1 to -6 %,
+  // N2048 -9 to -11 %, B4 H32 d64 causal N2048 -17 %, N4096 -10 %.
   switch (s.d) {
-    case 64: return c ? run<64, 64, 32, 8, true>(p, s.B, stage, st) : run<64, 64, 32, 8, false>(p, s.B, stage, st);
-    case 128: return c ? run<128, 64, 32, 8, true>(p, s.B, stage, st) : run<128, 64, 32, 8, false>(p, s.B, stage, st);
+    case 64: return c ? run<64, 64, 32, 4, true>(p, s.B, stage, st) : run<64, 64, 32, 4, false>(p, s.B, stage, st);
+    case 128: return c ? run<128, 64, 32, 4, true>(p, s.B, stage, st) : run<128, 64, 32, 4, false>(p, s.B, stage, st);
     case 256: return c ? run<256, 32, 32, 4, true>(p, s.B, stage, st) : run<256, 32, 32, 4, false>(p, s.B, stage, st);
     default: return hipErrorInvalidValue;
   }

@@ -1,7 +1,6 @@
 // The dQ kernel of the recompute backward (the first of its two kernels), for gfx950.
-// Included by bwd.hip (8-wave workgroups, and d = 256) and by bwd_dq_small.hip (the
-// 4-wave d = 64 and d = 128 kernels for small grids, built with a compiler option of
-// their own: see that file).
+// Included by bwd.hip (d = 256) and by bwd_dq_small.hip (d = 64 and 128, built with a
+// compiler option of their own: see that file); 4-wave workgroups at every head size.
 #pragma once
 #include "bwd_dkdv.h"
 
@@ -125,15 +124,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
     }
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
-        // (4-wave kernels: from one opaque LDS base, as their hoisted per-piece
-        // addresses spilled into vector lanes; the 8-wave ones were 1 % faster hoisted)
-        if constexpr (NW == 4) {
-          tile_load_full_o<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
-          tile_load_full_o<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
-        } else {
-          tile_load_full<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
-          tile_load_full<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
-        }
+        // (from one opaque LDS base: the hoisted per-piece addresses spilled into
+        // vector lanes)
+        tile_load_full_o<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
+        tile_load_full_o<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
         return;
       }
     }

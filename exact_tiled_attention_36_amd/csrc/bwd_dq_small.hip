@@ -1,9 +1,9 @@
-// dQ kernels for small grids (4 waves, d = 64 and 128) in a translation unit of their
-// own. build.py compiles this file with -mllvm --amdgpu-mfma-vgpr-form: the matrix
-// products write ordinary vector registers, so the softmax reads S and dP without a
-// v_accvgpr_read per element (a step of these kernels issues 193 vector instructions
-// instead of 257). The option is kept off the other dQ builds: it leaves the 8-wave
-// kernels unchanged and makes the d = 256 one spill.
+// dQ kernels for d = 64 and 128 (4 waves, 128 query rows per workgroup, two workgroups
+// per compute unit) in a translation unit of their own. build.py compiles this file with
+// -mllvm --amdgpu-mfma-vgpr-form: the matrix products write ordinary vector registers,
+// so the softmax reads S and dP without a v_accvgpr_read per element (a step of these
+// kernels issues 193 vector instructions instead of 257). The option is kept off the
+// d = 256 dQ build, which it makes spill.
 #include "bwd_dq.h"
 
 namespace fa {

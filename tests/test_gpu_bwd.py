@@ -96,7 +96,8 @@ def test_bwd_shapes(gpu_lib, shape):
 
 
 @pytest.mark.parametrize("shape", [
-    # at least 256 workgroups of 256 query rows: the 8-wave dQ kernel, ragged tails
+    # at least 256 workgroups of 256 query rows (large grids: many dQ workgroups per
+    # compute unit, dK/dV in 128-key workgroups), ragged tails
     (2, 32, 8, 1000, 1000, 128, True),
     (2, 32, 16, 1024, 1100, 64, False),
     # causal orders: dQ over 72 (batch, head) pairs (9 per XCD), dK/dV over 24 kv

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [
     # B, Hq, Hkv, Nq, Nk, d, causal
-    (2, 32, 8, 1000, 1000, 128, True),    # 4-wave forward, 8-wave dQ, dK/dV
+    (2, 32, 8, 1000, 1000, 128, True),    # 4-wave forward and dQ, dK/dV
     (1, 24, 24, 4200, 4300, 128, True),   # 8-wave forward
     (1, 8, 2, 700, 900, 128, True),       # small-grid forward and dQ, split dK/dV
     (2, 16, 16, 1024, 1024, 64, False),
