@@ -17,7 +17,7 @@ constexpr long long kSmallGrid = FWD_SMALL_GRID;
 #define FWD_PP128_MIN_ROWS 4096
 #endif
 constexpr int kPp128MinRows = FWD_PP128_MIN_ROWS;
-constexpr int kSmallKeys64 = 4096, kSmallKeys128 = 2048;
+constexpr int kSmallKeys64 = 4096, kSmallKeys128 = 3072;
 
 }  // namespace
 
@@ -63,8 +63,9 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   // of its 128-row workgroups share a compute unit (80 KB of LDS and 252 registers per
   // wave each), so one's start and end overlap the other's key loop. Measured against
   // the 8-wave kernel (B4 H32): d64 causal N2048 -11 %, N4096 -4 to -6 %, d64
-  // non-causal N4096 -3.5 %, d128 causal N2048 -5 %; but d128 causal N4096 +0-2 %, d128
-  // non-causal N4096 +14 %, N6144 d128 and N8192 d64 causal +2-3 %.
+  // non-causal N4096 -3.5 %, d128 causal N2048 -5 %, N3072 -3 %; but d128 causal N4096
+  // +0-2 %, d128 non-causal N2048 +3.5 % and N4096 +14 %, N6144 d128 and N8192 d64
+  // causal +2-3 %.
   if ((s.d == 64 && s.Nk <= kSmallKeys64) || (s.d == 128 && c && s.Nk <= kSmallKeys128))
     return launch_fwd_bf16_small(p, s.B, s.d, c, st);
   switch (s.d) {

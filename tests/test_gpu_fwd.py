@@ -64,7 +64,7 @@ def test_edge_shapes_bf16(gpu_lib, shape):
 
 
 # Grids of at least 256 workgroups of 256 query rows: the 4-wave (128-row) kernel up to
-# 4096 keys at d = 64 and up to 2048 keys for causal d = 128 (two of its workgroups per
+# 4096 keys at d = 64 and up to 3072 keys for causal d = 128 (two of its workgroups per
 # compute unit), else the 8-wave kernel (below the two-group kernel's range); the
 # shapes above are small grids, which take the 4-wave kernel too. Ragged key tails, GQA
 # and both causal alignments, compared element by element.
@@ -77,7 +77,7 @@ LARGE_GRID = [
     (3, 24, 8, 1000, 1000, 128, True),      # 4-wave
     (1, 68, 17, 1000, 1000, 64, True),      # 4-wave
     (1, 24, 24, 4200, 4300, 128, True),     # 8-wave; Nk > Nq, key tail
-    (1, 32, 32, 3000, 2500, 128, True),     # 8-wave; Nq > Nk
+    (1, 32, 32, 3600, 3300, 128, True),     # 8-wave; Nq > Nk
     (1, 17, 17, 4400, 4400, 64, True),      # 8-wave; 17 heads: level-major order
     (1, 16, 4, 4500, 4100, 64, False),      # 8-wave; d = 64 non-causal, Nq > Nk
 ]
