@@ -36,12 +36,18 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   if (wg256 < kSmallGrid && (s.d == 64 || s.d == 128)) {
     return launch_fwd_bf16_small(p, s.B, s.d, c, st);
   }
-  // d = 256: the two wave groups take turns on the matrix cores (fwd_pp.h), two waves
-  // per SIMD; measured 1.7x the one-wave-per-SIMD software-pipelined kernel (B2 H16
-  // N4096 causal: 490 -> 285 us). At d <= 128 a key tile's softmax takes about as long
-  // as its products, and the software-pipelined kernel below is 6-7 % faster.
-  if (s.d == 256)
-    return c ? run_pp<256, 32, true>(p, s.B, st) : run_pp<256, 32, false>(p, s.B, st);
+  // d = 256 (fwd_pp.h): two waves per SIMD, each alternating a matrix phase and a
+  // vector phase; measured 1.7x the one-wave-per-SIMD software-pipelined kernel (B2 H16
+  // N4096 causal: 490 -> 285 us). Causal and on small grids as 4-wave workgroups, two per
+  // compute unit (B2 H16 N4096 causal -1.5 to -3 %, B4 H16 N2048 -8 %, B1 H4 N1024
+  // -23 %); non-causal on large grids as 8-wave workgroups whose two groups take turns
+  // on the matrix cores (2 % faster there). At d <= 128 a key tile's softmax takes about
+  // as long as its products, and the software-pipelined kernel below is 6-7 % faster.
+  if (s.d == 256) {
+    if (c) return run_pp<256, 32, true, 1, false, 4>(p, s.B, st);
+    if (wg256 < kSmallGrid) return run_pp<256, 32, false, 1, false, 4>(p, s.B, st);
+    return run_pp<256, 32, false, 1, false, 8>(p, s.B, st);
+  }
   // d = 128 from 4096 query rows: the two-group kernel with two 32-row query blocks per
   // wave (fwd_pp.h), so each K / V^T operand read from LDS feeds two products, when it
   // still gives every compute unit a workgroup.

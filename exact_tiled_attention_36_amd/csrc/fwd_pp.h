@@ -26,6 +26,10 @@
 // step's end barrier. Each wave needs only one score tile and one packed-weight tile
 // per query block in registers (no in-wave software pipeline).
 //
+// NW = 4: one group of 4 waves (no turn-taking; 128 rows per workgroup at QB = 1): two
+// workgroups share a compute unit (72 KB of LDS each at d = 256), so each SIMD still
+// holds two waves, of different workgroups, that overlap by themselves.
+//
 // QB = 1 (d = 256): 32 rows per wave, Q in registers.
 // QB = 2 (d = 128, large grids): 64 rows per wave, 512 per workgroup, so every K or
 // V^T operand read from LDS feeds two products instead of one (LDS bytes per product
@@ -54,10 +58,10 @@ namespace {
 // no special case (its weights are exp2(-inf) = 0, its first rescale factor 0)
 constexpr float kNoMax = -1e30f;
 
-template <int D, int BN, bool CAUSAL, int QB, bool HP = false>
-__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
+template <int D, int BN, bool CAUSAL, int QB, bool HP = false, int NW = 8>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdParams p) {
   using TL = TileLayout<D>;
-  constexpr int NW = 8;
+  static_assert(NW == 8 || NW == 4, "two wave groups of 4, or one group of 4 waves");
   static_assert(!HP || QB == 2, "head pairs take two query blocks");
   // HP: the two blocks of a wave are the same 32 rows of two query heads that share a
   // kv-head; otherwise QB consecutive 32-row blocks of one head
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool grp_b = wu >= 4;   // wave-uniform
+  const bool grp_b = NW == 8 && wu >= 4;   // wave-uniform
   const int l32 = lane & 31, hi = lane >> 5;
 
   int qb, bh;
@@ -145,10 +149,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   const uint32_t lane_off = 4u * lane;
   auto load8 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
     if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
-      tile_load_full<D, BN, 8>(G, t * BN, dst, wu, lane_off);
+      tile_load_full<D, BN, NW>(G, t * BN, dst, wu, lane_off);
       return;
     }
-    tile_load_async<D, BN, 8>(G, t * BN, p.Nk, dst, wu, lane);
+    tile_load_async<D, BN, NW>(G, t * BN, p.Nk, dst, wu, lane);
   };
   auto load4 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {  // group A only
     if ((t + 1) * BN <= p.Nk) {
@@ -371,13 +375,13 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BN, bool CAUSAL, int QB = 1, bool HP = false>
+template <int D, int BN, bool CAUSAL, int QB = 1, bool HP = false, int NW = 8>
 hipError_t run_pp(FwdParams p, long long B, hipStream_t st) {
-  constexpr int BM = HP ? 256 : 256 * QB;
+  constexpr int BM = (HP ? 32 : 32 * QB) * NW;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * (HP ? p.Hq / 2 : p.Hq) * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL, QB, HP>), dim3((int)nb), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL, QB, HP, NW>), dim3((int)nb), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 

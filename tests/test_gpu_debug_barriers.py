@@ -20,7 +20,8 @@ SHAPES = [
     (1, 24, 24, 4200, 4300, 128, True),   # 8-wave forward
     (1, 8, 2, 700, 900, 128, True),       # small-grid forward and dQ, split dK/dV
     (2, 16, 16, 1024, 1024, 64, False),
-    (1, 8, 2, 520, 520, 256, True),       # two-group d = 256 forward
+    (1, 8, 2, 520, 520, 256, True),       # 4-wave d = 256 forward
+    (1, 32, 8, 2100, 2000, 256, False),   # two-group d = 256 forward
     (1, 32, 16, 8200, 8200, 128, True),   # two-group d = 128 forward, head pairs
     (1, 32, 32, 8200, 8200, 128, True),   # two-group d = 128 forward, 64 rows per wave
 ]
