@@ -80,9 +80,11 @@ LARGE_GRID = [
     (1, 32, 32, 3600, 3300, 128, True),     # 8-wave; Nq > Nk
     (1, 17, 17, 4400, 4400, 64, True),      # 8-wave; 17 heads: level-major order
     (1, 16, 4, 4500, 4100, 64, False),      # 8-wave; d = 64 non-causal, Nq > Nk
+    (2, 32, 8, 1500, 1700, 64, False),      # 4-wave; d = 64 non-causal, Nk > Nq
     # d = 256: 4-wave workgroups (causal), two wave groups of 4 (non-causal)
     (2, 16, 4, 2100, 2300, 256, True),
     (1, 32, 8, 2100, 2000, 256, False),
+    (1, 40, 1, 2000, 1800, 256, True),      # MQA, Nq > Nk: the first rows see no key
 ]
 
 
