@@ -38,8 +38,8 @@
 //
 // This header holds the kernel and its launch template; fwd_bf16.hip launches it
 // (8-wave workgroups, d = 64 and 128; d = 256 goes to fwd_pp.h) and
-// fwd_bf16_small.hip launches the 4-wave small-grid forms with a compiler option of
-// their own.
+// fwd_bf16_small.hip launches the 4-wave forms (small grids and short key ranges, two
+// workgroups per compute unit) with a compiler option of their own.
 #pragma once
 #include "common.h"
 #include "kernels.h"

@@ -1,6 +1,7 @@
-// Forward attention, bf16, 4-wave (128-row) workgroups for grids too small to give
-// every compute unit a 256-row workgroup (short sequences, few heads), d = 64 or 128,
-// in a translation unit of its own.
+// Forward attention, bf16, 4-wave (128-row) workgroups, d = 64 or 128, in a translation
+// unit of its own: for grids too small to give every compute unit a 256-row workgroup
+// (short sequences, few heads), and for short key ranges (two of these workgroups share
+// a compute unit; see fwd_bf16.hip).
 //
 // These kernels keep O in the accumulation registers, so the compiler also puts every
 // score product there and copies each element out before the softmax
