@@ -13,10 +13,9 @@ namespace {
 #define FWD_SMALL_GRID 256
 #endif
 constexpr long long kSmallGrid = FWD_SMALL_GRID;
-#ifndef FWD_PP128_MIN_ROWS
-#define FWD_PP128_MIN_ROWS 4096
-#endif
-constexpr int kPp128MinRows = FWD_PP128_MIN_ROWS;
+// query rows from which the d = 128 two-group kernel runs: head pairs causal, 64 rows of
+// one head causal, either form non-causal
+constexpr int kHpMinRowsCausal = 3072, kRowsMinRowsCausal = 8192, kPpMinRowsNonCausal = 1024;
 constexpr int kSmallKeys64 = 4096, kSmallKeys128 = 3072;
 
 }  // namespace
@@ -48,22 +47,25 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
     if (wg256 < kSmallGrid) return run_pp<256, 32, false, 1, false, 4>(p, s.B, st);
     return run_pp<256, 32, false, 1, false, 8>(p, s.B, st);
   }
-  // d = 128 from 4096 query rows: the two-group kernel with two 32-row query blocks per
-  // wave (fwd_pp.h), so each K / V^T operand read from LDS feeds two products, when it
-  // still gives every compute unit a workgroup.
+  // d = 128, long enough sequences: the two-group kernel with two 32-row query blocks
+  // per wave (fwd_pp.h), so each K / V^T operand read from LDS feeds two products, when
+  // it still gives every compute unit a workgroup.
   //  - an even number of query heads per kv-head: the two blocks are the same rows of
-  //    two heads of one group (256-row workgroups). Time against the kernel below: B2
+  //    two heads of one group (256-row workgroups). Time against the other kernels: B2
   //    Hq32 Hkv8 N8192 causal -8 % (-3.7 % against 64 consecutive rows), B4 Hq32 Hkv8
-  //    N4096 causal -11 %.
+  //    N4096 causal -11 %, N3072 -7 %, non-causal N2048 -8.5 %, B8 Hq32 Hkv8 N1024
+  //    non-causal -7.6 %; but causal N2048 +3.4 % (against the 4-wave kernel).
   //  - otherwise 64 consecutive rows of one head (512-row workgroups): B1 H8 N32768
-  //    causal -8 %, B2 H32 N4096 and B1 H8 N16384 non-causal -9 %, but B4 H32 N4096
-  //    causal +1 % (a 512-row workgroup walks the diagonal tiles for all of its rows, a
-  //    larger share of the work there), so causal from 8192 rows only.
+  //    causal -8 %, B2 H32 N4096 and B1 H8 N16384 non-causal -9 %, B8 H32 N2048 and B16
+  //    H32 N1024 non-causal -9 %, but B4 H32 N4096 causal +1 % (a 512-row workgroup walks
+  //    the diagonal tiles for all of its rows, a larger share of the work there), so
+  //    causal from 8192 rows only.
   const long long wghp = (long long)((s.Nq + 255) / 256) * (s.Hq / 2) * s.B;
-  if (s.d == 128 && (s.Hq / s.Hkv) % 2 == 0 && s.Nq >= kPp128MinRows && wghp >= kSmallGrid)
+  if (s.d == 128 && (s.Hq / s.Hkv) % 2 == 0 && s.Nq >= (c ? kHpMinRowsCausal : kPpMinRowsNonCausal) &&
+      wghp >= kSmallGrid)
     return c ? run_pp<128, 32, true, 2, true>(p, s.B, st) : run_pp<128, 32, false, 2, true>(p, s.B, st);
   const long long wg512 = (long long)((s.Nq + 511) / 512) * s.Hq * s.B;
-  if (s.d == 128 && s.Nq >= (c ? 2 * kPp128MinRows : kPp128MinRows) && wg512 >= kSmallGrid)
+  if (s.d == 128 && s.Nq >= (c ? kRowsMinRowsCausal : kPpMinRowsNonCausal) && wg512 >= kSmallGrid)
     return c ? run_pp<128, 32, true, 2>(p, s.B, st) : run_pp<128, 32, false, 2>(p, s.B, st);
   // For short key ranges the 4-wave kernel is also the faster one on large grids: two
   // of its 128-row workgroups share a compute unit (80 KB of LDS and 252 registers per

@@ -96,10 +96,11 @@ def test_large_grid_shapes_bf16(gpu_lib, shape):
     check_full(gpu_lib, inp, f"large{shape}")
 
 
-# d = 128 from 4096 query rows (with at least 256 workgroups) runs the two-group kernel
-# with two 32-row query blocks per wave: the same rows of two query heads of one group
-# when a kv-head has an even number of query heads ("pairs"), else 64 consecutive rows
-# of one head (causal from 8192 rows). Ragged query and key tails, both causal alignments
+# d = 128 with enough query rows (with at least 256 workgroups) runs the two-group
+# kernel with two 32-row query blocks per wave: the same rows of two query heads of one
+# group when a kv-head has an even number of query heads ("pairs"; causal from 3072
+# rows), else 64 consecutive rows of one head (causal from 8192 rows); non-causal either
+# form from 1024 rows. Ragged query and key tails, both causal alignments
 # (Nq > Nk leaves the first rows with no visible key: O = 0, lse = -inf), GQA/MQA,
 # non-causal and large logits; whole heads compared with the oracle (the first, a
 # middle and the last head: the first and last XCD's shares).
@@ -114,6 +115,9 @@ PP128 = [
     (1, 32, 16, 5000, 4000, 128, True, 1.0),   # pairs; Nq > Nk
     (2, 16, 8, 4096, 4500, 128, True, 1.0),    # pairs; Nk > Nq, two batches
     (1, 64, 1, 4100, 4100, 128, True, 1.0),    # MQA (64 heads per kv-head): pairs
+    (4, 32, 8, 1100, 1300, 128, False, 1.0),   # pairs, non-causal, short
+    (2, 48, 48, 1500, 1200, 128, False, 1.0),  # rows, non-causal, short; Nq > Nk
+    (2, 32, 8, 3100, 3100, 128, True, 1.0),    # pairs, causal from 3072 rows
 ]
 
 
@@ -121,9 +125,9 @@ PP128 = [
 def test_pp128_shapes_bf16(gpu_lib, shape):
     B, Hq, Hkv, Nq, Nk, d, causal, qm = shape
     if (Hq // Hkv) % 2 == 0:
-        assert Nq >= 4096 and -(-Nq // 256) * (Hq // 2) * B >= 256
+        assert Nq >= (3072 if causal else 1024) and -(-Nq // 256) * (Hq // 2) * B >= 256
     else:
-        assert Nq >= (8192 if causal else 4096) and -(-Nq // 512) * Hq * B >= 256
+        assert Nq >= (8192 if causal else 1024) and -(-Nq // 512) * Hq * B >= 256
     inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, q_mult=qm,
                             seed=2500 + Nq + Nk + Hkv)
     what = f"pp128{shape}"
