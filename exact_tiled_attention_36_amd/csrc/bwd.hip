@@ -53,11 +53,13 @@ hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (stage == -1 || stage == 1) {
-    // Grids of fewer than 256 workgroups of 128 keys leave compute units idle: there
-    // each workgroup takes 64 keys, its two wave pairs splitting every query tile
-    // (d = 64, 128).
+    // Grids of at most 256 workgroups of 128 keys leave compute units idle (one
+    // workgroup each, and under a causal mask the first keys' workgroups take twice the
+    // average): there each workgroup takes 64 keys, its two wave pairs splitting every
+    // query tile (d = 64, 128). At exactly 256: B2 Hq32 Hkv8 N2048 causal -20 %, B1
+    // Hq32 Hkv8 N4096 -25 %; at 384 and 512 the 128-key form is mostly ahead.
     const long long wg128 = (long long)((p.Nk + 127) / 128) * p.Hkv * B;
-    const bool split = BMQ == 64 && wg128 < 256;
+    const bool split = BMQ == 64 && wg128 <= 256;
     const int bnk = split || D == 256 ? 64 : 128;
     const int nkb = (p.Nk + bnk - 1) / bnk;
     const long long n = (long long)nkb * p.Hkv * B;

@@ -54,20 +54,21 @@ SHAPES_D256 = [
 ]
 
 
-# Fewer than 256 workgroups of 128 keys: the dK/dV kernel's split form (64 keys per
+# At most 256 workgroups of 128 keys: the dK/dV kernel's split form (64 keys per
 # workgroup, two wave pairs per query tile); most SHAPES above take it too.
 SHAPES_SPLIT = [
     (1, 8, 8, 2048, 2048, 128, True),
     (1, 8, 2, 2000, 2000, 64, True),
     (2, 4, 4, 1000, 1500, 128, False),
     (1, 6, 3, 1500, 700, 128, True),
+    (1, 32, 8, 4000, 4090, 128, True),     # exactly 256 workgroups of 128 keys; GQA
 ]
 
 
 @pytest.mark.parametrize("shape", SHAPES_SPLIT)
 def test_bwd_split_dkdv(gpu_lib, shape):
     B, Hq, Hkv, Nq, Nk, d, causal = shape
-    assert -(-Nk // 128) * Hkv * B < 256
+    assert -(-Nk // 128) * Hkv * B <= 256
     inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, with_do=True,
                             seed=3600 + Nq + 5 * Nk + Hq)
     check(gpu_lib, inp, f"bwd-split{shape}")
