@@ -1,8 +1,8 @@
 // Forward attention, bf16: launches of the software-pipelined kernel in fwd_bf16.h
 // (d = 64, and d = 128 for shorter sequences: 8-wave workgroups) and of the two-group
-// kernel in fwd_pp.h (d = 256, and d = 128 for long sequences), and the first-version
-// comparison forms; small grids and short key ranges (d = 64, and causal d = 128) go
-// to the 4-wave kernels of fwd_bf16_small.hip.
+// kernel in fwd_pp.h (d = 256, and d = 128 for long sequences or, with GQA, from 2048
+// rows), and the first-version comparison forms; small grids and short key ranges
+// (d = 64, and causal d = 128) go to the 4-wave kernels of fwd_bf16_small.hip.
 #include "fwd_bf16.h"
 #include "fwd_pp.h"
 
@@ -13,9 +13,10 @@ namespace {
 #define FWD_SMALL_GRID 256
 #endif
 constexpr long long kSmallGrid = FWD_SMALL_GRID;
-// query rows from which the d = 128 two-group kernel runs: head pairs causal, 64 rows of
-// one head causal, either form non-causal
-constexpr int kHpMinRowsCausal = 3072, kRowsMinRowsCausal = 8192, kPpMinRowsNonCausal = 1024;
+// query rows from which the d = 128 two-group kernel runs: head pairs causal (as 4-wave
+// workgroups below kHp8MinRowsCausal), 64 rows of one head causal, either form non-causal
+constexpr int kHpMinRowsCausal = 2048, kHp8MinRowsCausal = 8192, kRowsMinRowsCausal = 8192,
+              kPpMinRowsNonCausal = 1024;
 constexpr int kSmallKeys64 = 4096, kSmallKeys128 = 3072;
 
 }  // namespace
@@ -54,7 +55,11 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   //    two heads of one group (256-row workgroups). Time against the other kernels: B2
   //    Hq32 Hkv8 N8192 causal -8 % (-3.7 % against 64 consecutive rows), B4 Hq32 Hkv8
   //    N4096 causal -11 %, N3072 -7 %, non-causal N2048 -8.5 %, B8 Hq32 Hkv8 N1024
-  //    non-causal -7.6 %; but causal N2048 +3.4 % (against the 4-wave kernel).
+  //    non-causal -7.6 %. Causal below 8192 rows as one group of 4 waves (128 rows of
+  //    each head, 80 KB of LDS, two workgroups per compute unit): against the 8-wave
+  //    form B4 Hq32 Hkv8 N3072 -3 %, N4096 -1.8 %, B2 N6144 -0.4 %, but B2 N8192
+  //    +1.8 % (and non-causal +1.5 to +2 %); B4 N2048 -1.4 % against the 32-row 4-wave
+  //    kernel.
   //  - otherwise 64 consecutive rows of one head (512-row workgroups): B1 H8 N32768
   //    causal -8 %, B2 H32 N4096 and B1 H8 N16384 non-causal -9 %, B8 H32 N2048 and B16
   //    H32 N1024 non-causal -9 %, but B4 H32 N4096 causal +1 % (a 512-row workgroup walks
@@ -62,8 +67,11 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   //    causal from 8192 rows only.
   const long long wghp = (long long)((s.Nq + 255) / 256) * (s.Hq / 2) * s.B;
   if (s.d == 128 && (s.Hq / s.Hkv) % 2 == 0 && s.Nq >= (c ? kHpMinRowsCausal : kPpMinRowsNonCausal) &&
-      wghp >= kSmallGrid)
-    return c ? run_pp<128, 32, true, 2, true>(p, s.B, st) : run_pp<128, 32, false, 2, true>(p, s.B, st);
+      wghp >= kSmallGrid) {
+    if (!c) return run_pp<128, 32, false, 2, true>(p, s.B, st);
+    return s.Nq >= kHp8MinRowsCausal ? run_pp<128, 32, true, 2, true>(p, s.B, st)
+                                     : run_pp<128, 32, true, 2, true, 4>(p, s.B, st);
+  }
   const long long wg512 = (long long)((s.Nq + 511) / 512) * s.Hq * s.B;
   if (s.d == 128 && s.Nq >= (c ? kRowsMinRowsCausal : kPpMinRowsNonCausal) && wg512 >= kSmallGrid)
     return c ? run_pp<128, 32, true, 2>(p, s.B, st) : run_pp<128, 32, false, 2>(p, s.B, st);

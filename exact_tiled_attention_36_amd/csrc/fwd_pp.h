@@ -26,9 +26,10 @@
 // step's end barrier. Each wave needs only one score tile and one packed-weight tile
 // per query block in registers (no in-wave software pipeline).
 //
-// NW = 4: one group of 4 waves (no turn-taking; 128 rows per workgroup at QB = 1): two
-// workgroups share a compute unit (72 KB of LDS each at d = 256), so each SIMD still
-// holds two waves, of different workgroups, that overlap by themselves.
+// NW = 4: one group of 4 waves (no turn-taking; 128 rows per workgroup at QB = 1, or
+// 128 rows of each of two heads with HP): two workgroups share a compute unit (72 KB of
+// LDS each at d = 256, 80 KB for d = 128 head pairs), so each SIMD still holds two
+// waves, of different workgroups, that overlap by themselves.
 //
 // QB = 1 (d = 256): 32 rows per wave, Q in registers.
 // QB = 2 (d = 128, large grids): 64 rows per wave, 512 per workgroup, so every K or

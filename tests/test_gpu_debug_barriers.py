@@ -23,6 +23,7 @@ SHAPES = [
     (1, 8, 2, 520, 520, 256, True),       # 4-wave d = 256 forward
     (1, 32, 8, 2100, 2000, 256, False),   # two-group d = 256 forward
     (1, 32, 16, 8200, 8200, 128, True),   # two-group d = 128 forward, head pairs
+    (2, 32, 8, 2100, 2200, 128, True),    # 4-wave d = 128 forward, head pairs
     (1, 32, 32, 8200, 8200, 128, True),   # two-group d = 128 forward, 64 rows per wave
 ]
 

@@ -98,9 +98,9 @@ def test_large_grid_shapes_bf16(gpu_lib, shape):
 
 # d = 128 with enough query rows (with at least 256 workgroups) runs the two-group
 # kernel with two 32-row query blocks per wave: the same rows of two query heads of one
-# group when a kv-head has an even number of query heads ("pairs"; causal from 3072
-# rows), else 64 consecutive rows of one head (causal from 8192 rows); non-causal either
-# form from 1024 rows. Ragged query and key tails, both causal alignments
+# group when a kv-head has an even number of query heads ("pairs"; causal from 2048
+# rows, as 4-wave workgroups below 8192), else 64 consecutive rows of one head (causal
+# from 8192 rows); non-causal either form from 1024 rows. Ragged query and key tails, both causal alignments
 # (Nq > Nk leaves the first rows with no visible key: O = 0, lse = -inf), GQA/MQA,
 # non-causal and large logits; whole heads compared with the oracle (the first, a
 # middle and the last head: the first and last XCD's shares).
@@ -117,7 +117,10 @@ PP128 = [
     (1, 64, 1, 4100, 4100, 128, True, 1.0),    # MQA (64 heads per kv-head): pairs
     (4, 32, 8, 1100, 1300, 128, False, 1.0),   # pairs, non-causal, short
     (2, 48, 48, 1500, 1200, 128, False, 1.0),  # rows, non-causal, short; Nq > Nk
-    (2, 32, 8, 3100, 3100, 128, True, 1.0),    # pairs, causal from 3072 rows
+    (2, 32, 8, 3100, 3100, 128, True, 1.0),    # pairs, 4-wave workgroups
+    (4, 32, 8, 2100, 2000, 128, True, 1.0),    # pairs, 4-wave, from 2048 rows; Nq > Nk
+    (2, 64, 16, 2048, 2300, 128, True, 1.0),   # pairs, 4-wave, exactly 2048 rows; Nk > Nq
+    (1, 32, 8, 7000, 7100, 128, True, 1.0),    # pairs, 4-wave, up to 8191 rows
 ]
 
 
@@ -125,7 +128,7 @@ PP128 = [
 def test_pp128_shapes_bf16(gpu_lib, shape):
     B, Hq, Hkv, Nq, Nk, d, causal, qm = shape
     if (Hq // Hkv) % 2 == 0:
-        assert Nq >= (3072 if causal else 1024) and -(-Nq // 256) * (Hq // 2) * B >= 256
+        assert Nq >= (2048 if causal else 1024) and -(-Nq // 256) * (Hq // 2) * B >= 256
     else:
         assert Nq >= (8192 if causal else 1024) and -(-Nq // 512) * Hq * B >= 256
     inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, q_mult=qm,
