@@ -149,11 +149,17 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 int fa_splitkv_default_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || Hq % Hkv) return 1;
-  // Aim for about four workgroups per compute unit (256 CUs) with at least 256 keys
-  // per chunk; never more chunks than keys allow.
+  // About 512 chunk workgroups (two per compute unit), each at least 1024 keys long
+  // with one query row per kv-head (vector chunk kernel) or 512 with several (matrix-
+  // core chunk kernel). Measured at d = 128 over split counts 1-256 (MI355X): within
+  // 5 % of the best count on eight decode shapes (B1-B64, 8-512 (batch, kv-head)
+  // groups, 2048-65536 keys); against four workgroups per compute unit and 256 keys:
+  // B8 H8 Nk32768 -2 %, B1 H8 Nk32768 -42 %, B1 Hq32 Hkv8 Nk65536 -16 %, B2 Hq64 Hkv8
+  // Nk32768 -7 %, B16 Hq32 Hkv4 Nk8192 unchanged.
   const long long groups = (long long)B * Hkv;
-  long long s = (1024 + groups - 1) / groups;
-  const long long by_len = (Nk + 255) / 256;
+  long long s = (512 + groups - 1) / groups;
+  const long long min_chunk = (long long)(Hq / Hkv) * Nq <= 1 ? 1024 : 512;
+  const long long by_len = Nk / min_chunk;
   if (s > by_len) s = by_len;
   if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
