@@ -50,6 +50,8 @@ def test_gqa_decode_full_size(gpu_lib):
     (1, 4, 1, 4, 2, 128, True, 2),          # Nq > Nk: rows that see no key
     (2, 16, 1, 1, 1000, 64, False, 5),      # MQA, 16 rows per kv head
     (1, 6, 3, 5, 333, 128, True, 3),        # 10 rows, ragged chunks and tiles
+    (1, 8, 8, 1, 32768, 128, True, 0),      # default: 32 chunks of 1024 keys (vector)
+    (1, 32, 8, 1, 20000, 128, True, 0),     # default: 39 chunks of 513 keys (matrix)
 ])
 def test_splitkv_shapes(gpu_lib, case):
     B, Hq, Hkv, Nq, Nk, d, causal, splits = case
