@@ -38,8 +38,9 @@
 //
 // This header holds the kernel and its launch template; fwd_bf16.hip launches it
 // (8-wave workgroups, d = 64 and 128; d = 256 goes to fwd_pp.h) and
-// fwd_bf16_small.hip launches the 4-wave forms (small grids and short key ranges, two
-// workgroups per compute unit) with a compiler option of their own.
+// fwd_bf16_small.hip launches the 128-row forms (small grids: 8 waves splitting the
+// keys; short key ranges: 4 waves, two workgroups per compute unit) with a compiler
+// option of their own.
 #pragma once
 #include "common.h"
 #include "kernels.h"
@@ -56,9 +57,10 @@ struct FwdParams {
   float scale_log2;
 };
 
-// 4-wave (128-row) forward for grids too small for one 256-row workgroup per compute
-// unit, d = 64 or 128 (fwd_bf16_small.hip).
-hipError_t launch_fwd_bf16_small(FwdParams p, long long B, int d, bool causal, hipStream_t st);
+// 128-row forward, d = 64 or 128 (fwd_bf16_small.hip): 4-wave workgroups, or with
+// key_split 8-wave workgroups whose two halves take half of the key tiles each.
+hipError_t launch_fwd_bf16_small(FwdParams p, long long B, int d, bool causal, bool key_split,
+                                 hipStream_t st);
 
 namespace {
 
@@ -83,21 +85,33 @@ struct BoolC {
 // POLY (ablation only): every eighth weight 2^x is computed by poly_exp2 on the FMA
 // units instead of v_exp_f32, the partial software exponential that the wiki lists
 // for FlashAttention-4 (核心技術), to move work off the transcendental unit.
-template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false, bool POLY = false>
+// KS = 2 (grids too small to fill the GPU): the NW waves form two groups
+// that own the same rows and take one half of the key tiles each, in LDS buffers of
+// their own (the key/value-block split of §四.3 inside one workgroup); at the end the
+// second group hands its O, running max and row sums to the first through LDS, which
+// merges them with the rescale rule of §二.2 before the one division. Each wave's
+// chain of dependent key tiles is half as long and every SIMD holds two waves.
+template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false, bool POLY = false,
+          int KS = 1>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   using TL = TileLayout<D>;
+  static_assert(KS == 1 || (KS == 2 && QS == 1 && !RENORM && NW == 8),
+                "the key split is a one-block form of 8 waves");
+  constexpr int WG = NW / KS;    // waves per key group
   constexpr int RPW = 32 * QS;   // query rows per wave
-  constexpr int BM = RPW * NW;   // query rows per workgroup
+  constexpr int BM = RPW * WG;   // query rows per workgroup
   constexpr int TILE = TL::elems(BN);
   constexpr int NKB = BN / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide chunks of d (reduction of S)
   constexpr int NCB = D / 32;    // 32-wide column blocks of O
   static_assert(TL::shifts_ok(BN), "LDS reads add row offsets as constants");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = KS == 1 ? 0 : wall / WG;  // key group (uniform)
+  const int wu = KS == 1 ? wall : wall % WG;  // wave within its group
   const int l32 = lane & 31, hi = lane >> 5;
 
   int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -134,14 +148,21 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
     const int lim = q0 + BM + p.causal_off;  // keys < lim may be visible to some row
     kend = lim < kend ? lim : kend;
   }
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int ntiles_all = kend > 0 ? (kend + BN - 1) / BN : 0;
   // tiles [0, tfull) are wholly visible to every row of the workgroup
-  int tfull = p.Nk / BN;
+  int tfull_all = p.Nk / BN;
   if (CAUSAL) {
     const int lim = q0 + p.causal_off + 1;  // keys < lim are visible to every row
-    tfull = min(tfull, lim > 0 ? lim / BN : 0);
+    tfull_all = min(tfull_all, lim > 0 ? lim / BN : 0);
   }
-  tfull = min(tfull, ntiles);
+  tfull_all = min(tfull_all, ntiles_all);
+  // KS = 2: group g takes global tiles [g*nh, g*nh + nh) as its local tiles 0..nh-1 (the
+  // second group's last one may lie past the keys: copied from the last key row and
+  // masked away). Both groups run the same steps (their barriers are shared): the
+  // unmasked loop covers the local tiles unmasked in both groups.
+  const int ntiles = KS == 1 ? ntiles_all : (ntiles_all + 1) / 2;
+  const int t0 = ks * ntiles;  // global index of local tile 0
+  const int tfull = KS == 1 ? tfull_all : min(min(tfull_all, ntiles), max(tfull_all - ntiles, 0));
 
   f32x16_t oacc[QS][NCB];
   float m[QS], lsum[QS], m_use[QS], alpha[QS];
@@ -156,26 +177,28 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   }
   const float c2 = p.scale_log2;
 
-  auto Kb = [&](int i) FA_INLINE { return smem + (i & 1) * TILE; };
-  auto Vb = [&](int i) FA_INLINE { return smem + (2 + (i & 1)) * TILE; };
+  auto Kb = [&](int i) FA_INLINE { return smem + (4 * ks + (i & 1)) * TILE; };
+  auto Vb = [&](int i) FA_INLINE { return smem + (4 * ks + 2 + (i & 1)) * TILE; };
   // Rows past the last key re-read the last key row: always finite, and masked to
   // zero weight before they can contribute (tiles past the end are never used).
   const uint32_t lane_off = 4u * lane;
-  auto load = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
+  // local tile t of this wave's key group (each group copies its own tiles)
+  auto load = [&](const uint16_t* G, int tl, uint16_t* dst) FA_INLINE {
+    const int t = t0 + tl;
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
         // the 4-wave and non-causal kernels keep too many scalar values for the
         // per-piece LDS addresses the compiler would hoist (they spilled into vector
         // lanes: small-grid d = 128 forward 10 % faster without); the causal 8-wave
         // kernels did not spill and keep the hoisted form (1-3 % faster there)
-        if constexpr (CAUSAL && NW == 8)
-          tile_load_full<D, BN, NW>(G, t * BN, dst, wu, lane_off);
+        if constexpr (CAUSAL && NW == 8 && KS == 1)
+          tile_load_full<D, BN, WG>(G, t * BN, dst, wu, lane_off);
         else
-          tile_load_full_o<D, BN, NW>(G, t * BN, dst, wu, lane_off);
+          tile_load_full_o<D, BN, WG>(G, t * BN, dst, wu, lane_off);
         return;
       }
     }
-    tile_load_async<D, BN, NW>(G, t * BN, p.Nk, dst, wu, lane);
+    tile_load_async<D, BN, WG>(G, t * BN, p.Nk, dst, wu, lane);
   };
 
   // per-lane LDS byte offsets inside a tile: K operand rows, V^T transposed reads
@@ -228,9 +251,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
       }
   };
 
-  // causal / key-tail mask of the scores of tile t
+  // causal / key-tail mask of the scores of local tile t
   auto mask = [&](f32x16_t (&sc)[QS][NKB], int t) FA_INLINE {
-    const int j0 = t * BN;
+    const int j0 = (t0 + t) * BN;
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       const int lim = CAUSAL ? w0 + 32 * qs + l32 + p.causal_off : 0x7fffffff;
@@ -384,6 +407,33 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
     }
   }
 
+  if constexpr (KS == 2) {
+    // the second key group's O, base m and row sums to the first (tile buffers free:
+    // every wave is past its last step)
+    constexpr int XF = NCB * 16 + 2;  // floats per lane
+    float* xf = (float*)smem + (size_t)wu * XF * 64 + lane;
+    __syncthreads();
+    if (ks == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xf[(16 * cb + r) * 64] = oacc[0][cb][r];
+      xf[(NCB * 16) * 64] = m[0];
+      xf[(NCB * 16 + 1) * 64] = lsum[0];
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    const float m1 = xf[(NCB * 16) * 64], l1 = xf[(NCB * 16 + 1) * 64];
+    const float mt = fmaxf(m[0], m1);
+    const float mb = mt == -INFINITY ? 0.f : mt;
+    const float a0 = fast_exp2(m[0] - mb), a1 = fast_exp2(m1 - mb);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[0][cb][r] = oacc[0][cb][r] * a0 + xf[(16 * cb + r) * 64] * a1;
+    lsum[0] = lsum[0] * a0 + l1 * a1;
+    m[0] = mt;
+  }
   // Epilogue: combine the two half-row sums, normalise once, store O and LSE.
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
@@ -409,13 +459,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false, bool POLY = false>
+template <int D, int BN, int NW, int QS, bool CAUSAL, bool RENORM = false, bool POLY = false,
+          int KS = 1>
 hipError_t run(FwdParams p, long long B, hipStream_t st) {
-  constexpr int BM = 32 * NW * QS;
+  constexpr int BM = 32 * (NW / KS) * QS;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * p.Hq * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, QS, CAUSAL, RENORM, POLY>), dim3((int)nb), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, QS, CAUSAL, RENORM, POLY, KS>), dim3((int)nb),
+                     dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
 // Forward attention, bf16: launches of the software-pipelined kernel in fwd_bf16.h
 // (d = 64, and d = 128 for shorter sequences: 8-wave workgroups) and of the two-group
 // kernel in fwd_pp.h (d = 256, and d = 128 for long sequences or, with GQA, from 2048
-// rows), and the first-version comparison forms; small grids and short key ranges
-// (d = 64, and causal d = 128) go to the 4-wave kernels of fwd_bf16_small.hip.
+// rows), and the first-version comparison forms; small grids (the key-split form) and
+// short key ranges (d = 64, and causal d = 128: 4-wave workgroups) go to the 128-row
+// kernels of fwd_bf16_small.hip.
 #include "fwd_bf16.h"
 #include "fwd_pp.h"
 
@@ -30,11 +31,15 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   p.scale_log2 = s.scale * kLog2e;
   const bool c = s.causal != 0;
   // Grids too small to give every compute unit a 256-row workgroup (short sequences,
-  // few heads) use 128-row workgroups of 4 waves instead: twice the workgroups, each
-  // less efficient per unit of work, but no compute unit left idle.
+  // few heads) use 128-row workgroups instead: twice the workgroups, each less
+  // efficient per unit of work, but no compute unit left idle. Each has 8 waves in two
+  // groups that take half of the key tiles each (fwd_bf16.h, KS = 2), so every SIMD
+  // holds two waves and a wave's chain of key tiles is half as long; against 4-wave
+  // workgroups over all keys: B2 H16 N1024 d64 non-causal -14 %, B1 H8 N2048 d64 -22 %
+  // (causal -27 %), d128 -11 % (causal -13 %), B2 H8 N1024 d128 causal -9 %.
   const long long wg256 = (long long)((s.Nq + 255) / 256) * s.Hq * s.B;
   if (wg256 < kSmallGrid && (s.d == 64 || s.d == 128)) {
-    return launch_fwd_bf16_small(p, s.B, s.d, c, st);
+    return launch_fwd_bf16_small(p, s.B, s.d, c, true, st);
   }
   // d = 256 (fwd_pp.h): two waves per SIMD, each alternating a matrix phase and a
   // vector phase; measured 1.7x the one-wave-per-SIMD software-pipelined kernel (B2 H16
@@ -83,7 +88,7 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   // +0-2 %, d128 non-causal N2048 +3.5 % and N4096 +14 %, N6144 d128 and N8192 d64
   // causal +2-3 %.
   if ((s.d == 64 && s.Nk <= kSmallKeys64) || (s.d == 128 && c && s.Nk <= kSmallKeys128))
-    return launch_fwd_bf16_small(p, s.B, s.d, c, st);
+    return launch_fwd_bf16_small(p, s.B, s.d, c, false, st);
   switch (s.d) {
 #ifndef FWD_CFG128
 #define FWD_CFG128 64, 8, 1

@@ -1,7 +1,8 @@
-// Forward attention, bf16, 4-wave (128-row) workgroups, d = 64 or 128, in a translation
-// unit of its own: for grids too small to give every compute unit a 256-row workgroup
-// (short sequences, few heads), and for short key ranges (two of these workgroups share
-// a compute unit; see fwd_bf16.hip).
+// Forward attention, bf16, 128-row workgroups, d = 64 or 128, in a translation unit of
+// its own: for grids too small to give every compute unit a 256-row workgroup (short
+// sequences, few heads) as 8 waves whose two halves take half of the key tiles each,
+// and for short key ranges as 4 waves (two of these workgroups share a compute unit;
+// see fwd_bf16.hip).
 //
 // These kernels keep O in the accumulation registers, so the compiler also puts every
 // score product there and copies each element out before the softmax
@@ -15,7 +16,17 @@
 
 namespace fa {
 
-hipError_t launch_fwd_bf16_small(FwdParams p, long long B, int d, bool causal, hipStream_t st) {
+hipError_t launch_fwd_bf16_small(FwdParams p, long long B, int d, bool causal, bool key_split,
+                                 hipStream_t st) {
+  if (key_split) {
+    if (d == 64)
+      return causal ? run<64, 64, 8, 1, true, false, false, 2>(p, B, st)
+                    : run<64, 64, 8, 1, false, false, false, 2>(p, B, st);
+    if (d == 128)
+      return causal ? run<128, 64, 8, 1, true, false, false, 2>(p, B, st)
+                    : run<128, 64, 8, 1, false, false, false, 2>(p, B, st);
+    return hipErrorInvalidValue;
+  }
   if (d == 64) return causal ? run<64, 64, 4, 1, true>(p, B, st) : run<64, 64, 4, 1, false>(p, B, st);
   if (d == 128) return causal ? run<128, 64, 4, 1, true>(p, B, st) : run<128, 64, 4, 1, false>(p, B, st);
   return hipErrorInvalidValue;

@@ -18,7 +18,8 @@ SHAPES = [
     # B, Hq, Hkv, Nq, Nk, d, causal
     (2, 32, 8, 1000, 1000, 128, True),    # 4-wave forward and dQ, dK/dV
     (1, 24, 24, 4200, 4300, 128, True),   # 8-wave forward
-    (1, 8, 2, 700, 900, 128, True),       # small-grid forward and dQ, split dK/dV
+    (1, 8, 2, 700, 900, 128, True),       # small-grid forward (key split) and dQ, split dK/dV
+    (1, 4, 4, 300, 130, 64, False),       # key-split forward, odd key-tile count
     (2, 16, 16, 1024, 1024, 64, False),
     (1, 8, 2, 520, 520, 256, True),       # 4-wave d = 256 forward
     (1, 32, 8, 2100, 2000, 256, False),   # two-group d = 256 forward

@@ -53,6 +53,10 @@ EDGE = [
     (1, 8, 1, 129, 511, 64, True),          # MQA
     (1, 2, 1, 300, 100, 64, True),          # Nq > Nk: first rows see no key
     (2, 2, 2, 1, 700, 128, True),           # decode-like through the tiled kernel
+    # small grids run 128-row workgroups whose two wave groups take half of the key
+    # tiles each: odd tile counts (the second group's last tile lies past the keys)
+    (1, 8, 4, 500, 130, 64, False), (1, 4, 1, 900, 700, 64, True),
+    (3, 4, 4, 640, 640, 128, False), (1, 6, 3, 450, 1500, 128, True),
 ]
 
 
