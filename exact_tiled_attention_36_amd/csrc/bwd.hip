@@ -12,7 +12,8 @@
 //
 // Two kernels on one stream:
 //  1. bwd_dq (bwd_dq.h; first): one workgroup per (batch, head, 128 queries: 4 waves of
-//     32; d = 64 and 128 from bwd_dq_small.hip); Q and dO stay in registers, K/V tiles are triple
+//     32, or on small grids 8 waves in two groups that split the key tiles; d = 64 and
+//     128 from bwd_dq_small.hip); Q and dO stay in registers, K/V tiles are triple
 //     buffered in LDS; S^T and dP^T put one query per lane, so LSE and D are per-lane
 //     scalars, and dQ^T += K^T dS^T reads K^T with LDS transpose loads. Its prologue
 //     forms D_i from its rows of O and dO (dO is in registers already) and stores D
@@ -36,6 +37,13 @@
 namespace fa {
 namespace {
 
+// dQ grids of at most this many 128-row workgroups (two per compute unit fill 512) run
+// the key-split form (bwd_dq.h, KS = 2: 8 waves, two groups taking half of the key
+// tiles each). Against the 4-wave form: B1 H8 N2048 d128 causal -11 % (128
+// workgroups), B1 H16 -7 %, B4 H8 N1024 d64 causal -10 % (256), B1 H24 -14 % (384),
+// B1 H32 N2048 -19 % (512); but B2 H24 N2048 +10 % (768) and +5 to +20 % at 1024.
+constexpr long long kDqKeySplitMaxGrid = 512;
+
 // stage 0: dQ (and D, LSE * log2(e) into the workspace); stage 1: dK, dV; stage -1: both.
 template <int D, int BMQ, int BN, int NWQ, bool CAUSAL>
 hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
@@ -45,7 +53,7 @@ hipError_t run(const BwdParams& p, int B, int stage, hipStream_t st) {
     if (n > 0x7fffffffLL) return hipErrorInvalidValue;
     hipError_t e;
     if constexpr (NWQ == 4 && D <= 128) {
-      e = launch_bwd_dq_small(p, nqb, (int)n, D, CAUSAL, st);
+      e = launch_bwd_dq_small(p, nqb, (int)n, D, CAUSAL, n <= kDqKeySplitMaxGrid, st);
     } else {
       hipLaunchKernelGGL((bwd_dq_kernel<D, BN, NWQ, CAUSAL>), dim3((int)n), dim3(64 * NWQ), 0, st, p, nqb);
       e = hipGetLastError();

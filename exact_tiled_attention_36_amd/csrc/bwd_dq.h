@@ -6,10 +6,11 @@
 
 namespace fa {
 
-// Launch of bwd_dq_kernel<d, 32, 4, causal> (d = 64 or 128) on `grid` workgroups
-// (bwd_dq_small.hip).
+// Launch of bwd_dq_kernel<d, 32, 4, causal> (d = 64 or 128) on `grid` workgroups, or
+// with key_split of its 8-wave form whose two wave groups take half of the key tiles
+// each (bwd_dq_small.hip).
 hipError_t launch_bwd_dq_small(const BwdParams& p, int nqb, int grid, int d, bool causal,
-                               hipStream_t st);
+                               bool key_split, hipStream_t st);
 
 namespace {
 // ---------------------------------------------------------------------------------
@@ -23,19 +24,29 @@ namespace {
 // then the copies' wait and a barrier. S^T and dP^T put one query per lane, so LSE
 // and D are per-lane scalars; dS^T comes out in the B-operand layout of the dQ
 // product, and K^T is read with LDS transpose loads.
-template <int D, int BN, int NW, bool CAUSAL>
+//
+// KS = 2 (grids too small to fill the GPU): the NW waves form two groups that own the
+// same rows and take one half of the key tiles each, in LDS buffers of their own; at
+// the end the second group adds its partial dQ into the first's through LDS (dQ is a
+// plain sum over key tiles). Each wave's chain of key tiles is half as long and every
+// SIMD holds two waves.
+template <int D, int BN, int NW, bool CAUSAL, int KS = 1>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb) {
   using TL = TileLayout<D>;
   constexpr int TILE = TL::elems(BN);
   constexpr int NDC = D / 16, NCB = D / 32, NKB = BN / 32;
-  constexpr int BM = 32 * NW;    // query rows per workgroup (one 32-row block per wave)
+  static_assert(KS == 1 || (KS == 2 && D <= 128 && NW == 8), "the key split is an 8-wave form");
+  constexpr int WG = NW / KS;    // waves per key group
+  constexpr int BM = 32 * WG;    // query rows per workgroup (one 32-row block per wave)
   constexpr int NB = 3;
   static_assert(TL::shifts_ok(BN), "LDS reads add row offsets as constants");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NB * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * NB * 2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = KS == 1 ? 0 : wall / WG;     // key group (uniform)
+  const int wu = KS == 1 ? wall : wall % WG;  // wave within its group
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int qb, bh;
@@ -83,7 +94,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
   const float lraw = p.lse[rowidx];
   const float Dv = qvalid ? dsum : 0.f;
   const float lse2 = (!qvalid || lraw == -INFINITY) ? INFINITY : lraw * kLog2e;
-  if (qvalid && hi == 0) {
+  if (qvalid && hi == 0 && ks == 0) {
     p.dvec[rowidx] = Dv;
     p.lse2v[rowidx] = lse2;
   }
@@ -97,42 +108,52 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
     const int lim = q0 + BM + p.causal_off;
     kend = lim < kend ? lim : kend;
   }
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int ntiles_all = kend > 0 ? (kend + BN - 1) / BN : 0;
   // tiles [0, tfull) are wholly visible to every row of the workgroup
-  int tfull = p.Nk / BN;
+  int tfull_all = p.Nk / BN;
   if (CAUSAL) {
     const int lim = q0 + p.causal_off + 1;
-    tfull = min(tfull, lim > 0 ? lim / BN : 0);
+    tfull_all = min(tfull_all, lim > 0 ? lim / BN : 0);
   }
-  tfull = min(tfull, ntiles);
+  tfull_all = min(tfull_all, ntiles_all);
+  // KS = 2: group g takes global tiles [g*nh, g*nh + nh) as its local tiles 0..nh-1 (the
+  // second group's last one may lie past the keys: copied from the last key row and
+  // masked away). Both groups run the same steps (their barriers are shared): the
+  // unmasked loop covers the local tiles unmasked in both groups.
+  const int ntiles = KS == 1 ? ntiles_all : (ntiles_all + 1) / 2;
+  const int t0 = ks * ntiles;  // global index of local tile 0
+  const int tfull = KS == 1 ? tfull_all : min(min(tfull_all, ntiles), max(tfull_all - ntiles, 0));
 
   f32x16_t dqacc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dqacc[cb] = zero16();
   const float c2 = p.scale_log2;
 
-  // buffer t%3 holds the K tile of key tile t, followed by its V tile
-  auto Kb = [&](int t) FA_INLINE { return smem + (t % NB) * 2 * TILE; };
+  // buffer t%3 (of this wave's key group) holds the K tile of local key tile t, followed
+  // by its V tile
+  auto Kb = [&](int t) FA_INLINE { return smem + (ks * NB + t % NB) * 2 * TILE; };
   // rows past Nk re-read the last key row; the key-tail mask zeroes their weight
   const uint32_t lane_off = 4u * lane;
-  auto load_tile = [&](int t) FA_INLINE {
+  auto load_tile = [&](int tl) FA_INLINE {
+    const int t = t0 + tl;
+    uint16_t* const buf = Kb(tl);
     if constexpr (D == 256) {
-      const uint32_t m0 = lds_addr(Kb(t));
-      tile_load_m0<D, BN, NW>(Kg, t * BN, p.Nk, m0, wu, lane_off);
-      tile_load_m0<D, BN, NW>(Vg, t * BN, p.Nk, m0 + 2 * TILE, wu, lane_off);
+      const uint32_t m0 = lds_addr(buf);
+      tile_load_m0<D, BN, WG>(Kg, t * BN, p.Nk, m0, wu, lane_off);
+      tile_load_m0<D, BN, WG>(Vg, t * BN, p.Nk, m0 + 2 * TILE, wu, lane_off);
       return;
     }
     if constexpr (D <= 128) {
       if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
         // (from one opaque LDS base: the hoisted per-piece addresses spilled into
         // vector lanes)
-        tile_load_full_o<D, BN, NW>(Kg, t * BN, Kb(t), wu, lane_off);
-        tile_load_full_o<D, BN, NW>(Vg, t * BN, Kb(t) + TILE, wu, lane_off);
+        tile_load_full_o<D, BN, WG>(Kg, t * BN, buf, wu, lane_off);
+        tile_load_full_o<D, BN, WG>(Vg, t * BN, buf + TILE, wu, lane_off);
         return;
       }
     }
-    tile_load_async<D, BN, NW>(Kg, t * BN, p.Nk, Kb(t), wu, lane);
-    tile_load_async<D, BN, NW>(Vg, t * BN, p.Nk, Kb(t) + TILE, wu, lane);
+    tile_load_async<D, BN, WG>(Kg, t * BN, p.Nk, buf, wu, lane);
+    tile_load_async<D, BN, WG>(Vg, t * BN, p.Nk, buf + TILE, wu, lane);
   };
 
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
@@ -157,9 +178,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
         dP[kb] = mfma32x32x16(lds_read8_at(a + 2 * TILE), doreg[dc], dP[kb]);
       }
   };
-  // causal / key-tail mask of key tile t: masked scores give P = dS = 0
+  // causal / key-tail mask of local key tile t: masked scores give P = dS = 0
   auto mask = [&](f32x16_t (&S)[NKB], int t) FA_INLINE {
-    const int j0 = t * BN;
+    const int j0 = (t0 + t) * BN;
     const int lim = CAUSAL ? qrow + p.causal_off : 0x7fffffff;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -249,6 +270,24 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdParams p, int nqb
     }
   }
 
+  if constexpr (KS == 2) {
+    // the second key group's partial dQ into the first's (tile buffers free: every
+    // wave is past its last step)
+    float* xf = (float*)smem + (size_t)wu * (NCB * 16) * 64 + lane;
+    __syncthreads();
+    if (ks == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xf[(16 * cb + r) * 64] = dqacc[cb][r];
+    }
+    __syncthreads();
+    if (ks == 1) return;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[cb][r] += xf[(16 * cb + r) * 64];
+  }
   if (qvalid) {
     uint16_t* orow = p.dq + rowidx * D;
 #pragma unroll

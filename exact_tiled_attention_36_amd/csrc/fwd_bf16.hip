@@ -36,9 +36,11 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   // groups that take half of the key tiles each (fwd_bf16.h, KS = 2), so every SIMD
   // holds two waves and a wave's chain of key tiles is half as long; against 4-wave
   // workgroups over all keys: B2 H16 N1024 d64 non-causal -14 %, B1 H8 N2048 d64 -22 %
-  // (causal -27 %), d128 -11 % (causal -13 %), B2 H8 N1024 d128 causal -9 %.
+  // (causal -27 %), d128 -11 % (causal -13 %), B2 H8 N1024 d128 causal -9 %. Causal
+  // grids of exactly 256 such workgroups too (B1 H32 N2048 d128 -17 %, B2 H16 N2048 d64
+  // -25 %; non-causal there +15 %, causal d128 at 384 or 512 +9 to +14 %).
   const long long wg256 = (long long)((s.Nq + 255) / 256) * s.Hq * s.B;
-  if (wg256 < kSmallGrid && (s.d == 64 || s.d == 128)) {
+  if ((c ? wg256 <= kSmallGrid : wg256 < kSmallGrid) && (s.d == 64 || s.d == 128)) {
     return launch_fwd_bf16_small(p, s.B, s.d, c, true, st);
   }
   // d = 256 (fwd_pp.h): two waves per SIMD, each alternating a matrix phase and a

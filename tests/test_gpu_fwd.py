@@ -60,6 +60,28 @@ EDGE = [
 ]
 
 
+# Causal grids of exactly 256 workgroups of 256 rows also take the key-split form
+# (non-causal ones the 4-wave form); compared on whole heads: the first and the last.
+KS_EDGE = [(1, 32, 8, 2048, 2100, 128, True), (2, 16, 16, 2000, 2048, 64, True),
+           (1, 32, 32, 2048, 1900, 128, False)]
+
+
+@pytest.mark.parametrize("shape", KS_EDGE)
+def test_key_split_boundary_grids(gpu_lib, shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    assert -(-Nq // 256) * Hq * B == 256
+    inp = synth.make_inputs(B, Hq, Hkv, Nq, Nk, d, causal=causal, seed=3300 + Nq + Nk + d)
+    what = f"ks{shape}"
+    announce(f"fwd {what}")
+    o, lse = run_fwd(gpu_lib, inp)
+    assert np.all(np.isfinite(o))
+    qf, kf, vf = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
+    for b, h in ((0, 0), (B - 1, Hq - 1)):
+        o_ref, lse_ref = A.forward_head(qf, kf, vf, inp.scale, inp.causal, b, h)
+        assert_o_close(o[b, h], o_ref, f"{what} b{b} h{h}")
+        assert_lse_close(lse[b, h], lse_ref, TOL_LSE_BF16, f"{what} b{b} h{h}")
+
+
 @pytest.mark.parametrize("shape", EDGE)
 def test_edge_shapes_bf16(gpu_lib, shape):
     B, Hq, Hkv, Nq, Nk, d, causal = shape
