@@ -50,9 +50,14 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   // -23 %); non-causal on large grids as 8-wave workgroups whose two groups take turns
   // on the matrix cores (2 % faster there). At d <= 128 a key tile's softmax takes about
   // as long as its products, and the software-pipelined kernel below is 6-7 % faster.
+  // Small grids: two such 4-wave groups in one workgroup, each over half of the key
+  // tiles (fwd_pp.h KS = 2): B2 H8 N2048 causal -15 %, B1 Hq8 Hkv2 N4000 causal -18 %,
+  // B1 H4 N1024 -10 %, B2 H8 N2048 non-causal -6 %.
   if (s.d == 256) {
+    if (wg256 < kSmallGrid)
+      return c ? run_pp<256, 32, true, 1, false, 4, 2>(p, s.B, st)
+               : run_pp<256, 32, false, 1, false, 4, 2>(p, s.B, st);
     if (c) return run_pp<256, 32, true, 1, false, 4>(p, s.B, st);
-    if (wg256 < kSmallGrid) return run_pp<256, 32, false, 1, false, 4>(p, s.B, st);
     return run_pp<256, 32, false, 1, false, 8>(p, s.B, st);
   }
   // d = 128, long enough sequences: the two-group kernel with two 32-row query blocks

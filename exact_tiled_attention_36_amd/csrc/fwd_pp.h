@@ -59,10 +59,16 @@ namespace {
 // no special case (its weights are exp2(-inf) = 0, its first rescale factor 0)
 constexpr float kNoMax = -1e30f;
 
-template <int D, int BN, bool CAUSAL, int QB, bool HP = false, int NW = 8>
-__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdParams p) {
+//
+// KS = 2 (one-block 4-wave form, grids too small to fill the GPU): two such groups of 4
+// waves in one workgroup own the same rows and take one half of the key tiles each, in
+// LDS buffers of their own; at the end the second hands O, its base m and its row sums
+// to the first through LDS, which merges them (§二.2 rescale) before the one division.
+template <int D, int BN, bool CAUSAL, int QB, bool HP = false, int NW = 8, int KS = 1>
+__global__ __launch_bounds__(64 * NW * KS, (NW == 8 || KS == 2) ? 1 : 2) void fwd_pp_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   static_assert(NW == 8 || NW == 4, "two wave groups of 4, or one group of 4 waves");
+  static_assert(KS == 1 || (KS == 2 && NW == 4 && QB == 1 && !HP), "key split of the 4-wave form");
   static_assert(!HP || QB == 2, "head pairs take two query blocks");
   // HP: the two blocks of a wave are the same 32 rows of two query heads that share a
   // kv-head; otherwise QB consecutive 32-row blocks of one head
@@ -79,10 +85,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdPar
   // registers hold Q of the first block only
   constexpr int QT = TL::elems(32);
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (QB - 1) * NW * QT];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * (4 * TILE + (QB - 1) * NW * QT)];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = KS == 1 ? 0 : wall / NW;     // key group (uniform)
+  const int wu = KS == 1 ? wall : wall % NW;  // wave within its group
   const bool grp_b = NW == 8 && wu >= 4;   // wave-uniform
   const int l32 = lane & 31, hi = lane >> 5;
 
@@ -123,14 +131,20 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdPar
     const int lim = q0 + BM + p.causal_off;  // keys < lim may be visible to some row
     kend = lim < kend ? lim : kend;
   }
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int ntiles_all = kend > 0 ? (kend + BN - 1) / BN : 0;
   // tiles [0, tfull) are wholly visible to every row of the workgroup
-  int tfull = p.Nk / BN;
+  int tfull_all = p.Nk / BN;
   if (CAUSAL) {
     const int lim = q0 + p.causal_off + 1;  // keys < lim are visible to every row
-    tfull = min(tfull, lim > 0 ? lim / BN : 0);
+    tfull_all = min(tfull_all, lim > 0 ? lim / BN : 0);
   }
-  tfull = min(tfull, ntiles);
+  tfull_all = min(tfull_all, ntiles_all);
+  // KS = 2: group g takes global tiles [g*nh, g*nh + nh) as its local tiles 0..nh-1 (the
+  // second group's last one may lie past the keys: copied from the last key row and
+  // masked away); both groups run the same steps, since they share the barriers
+  const int ntiles = KS == 1 ? ntiles_all : (ntiles_all + 1) / 2;
+  const int t0 = ks * ntiles;  // global index of local tile 0
+  const int tfull = KS == 1 ? tfull_all : min(min(tfull_all, ntiles), max(tfull_all - ntiles, 0));
 
   f32x16_t oacc[QB][NCB];
   float m[QB], lsum[QB];  // running max (log2 units) and row sum per block
@@ -143,19 +157,21 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdPar
   }
   const float c2 = p.scale_log2;
 
-  auto Kb = [&](int i) FA_INLINE { return smem + (i & 1) * TILE; };
-  auto Vb = [&](int i) FA_INLINE { return smem + (2 + (i & 1)) * TILE; };
+  auto Kb = [&](int i) FA_INLINE { return smem + (4 * ks + (i & 1)) * TILE; };
+  auto Vb = [&](int i) FA_INLINE { return smem + (4 * ks + 2 + (i & 1)) * TILE; };
   // Rows past the last key re-read the last key row: always finite, and masked to
   // zero weight before they can contribute.
   const uint32_t lane_off = 4u * lane;
-  auto load8 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {
+  auto load8 = [&](const uint16_t* G, int tl, uint16_t* dst) FA_INLINE {
+    const int t = t0 + tl;
     if ((t + 1) * BN <= p.Nk) {  // whole tile present: scalar-addressed copies
       tile_load_full<D, BN, NW>(G, t * BN, dst, wu, lane_off);
       return;
     }
     tile_load_async<D, BN, NW>(G, t * BN, p.Nk, dst, wu, lane);
   };
-  auto load4 = [&](const uint16_t* G, int t, uint16_t* dst) FA_INLINE {  // group A only
+  auto load4 = [&](const uint16_t* G, int tl, uint16_t* dst) FA_INLINE {  // group A only
+    const int t = t0 + tl;
     if ((t + 1) * BN <= p.Nk) {
       tile_load_full<D, BN, 4>(G, t * BN, dst, wu, lane_off);
       return;
@@ -239,8 +255,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdPar
   auto vec_phase = [&](int j) FA_INLINE {
     if (j >= tfull) {  // causal diagonal or key tail
       // key j*BN + 4*hi + c (c a per-register constant) is visible to this lane's row
-      // iff c <= T, with T the last visible key less the lane's base
-      const int base = j * BN + 4 * hi;
+      // iff c <= T, with T the last visible key less the lane's base (j local)
+      const int base = (t0 + j) * BN + 4 * hi;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         int last = p.Nk - 1;
@@ -350,6 +366,32 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdPar
     }
   }
 
+  if constexpr (KS == 2) {
+    // the second key group's O, base m and row sums to the first (tile buffers free:
+    // every wave is past its last step)
+    constexpr int XF = NCB * 16 + 2;  // floats per lane
+    float* xf = (float*)smem + (size_t)wu * XF * 64 + lane;
+    __syncthreads();
+    if (ks == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xf[(16 * cb + r) * 64] = oacc[0][cb][r];
+      xf[(NCB * 16) * 64] = m[0];
+      xf[(NCB * 16 + 1) * 64] = lsum[0];
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    const float m1 = xf[(NCB * 16) * 64], l1 = xf[(NCB * 16 + 1) * 64];
+    const float mt = fmaxf(m[0], m1);  // both bases finite (kNoMax before any key)
+    const float a0 = fast_exp2(m[0] - mt), a1 = fast_exp2(m1 - mt);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[0][cb][r] = oacc[0][cb][r] * a0 + xf[(16 * cb + r) * 64] * a1;
+    lsum[0] = lsum[0] * a0 + l1 * a1;
+    m[0] = mt;
+  }
   // Epilogue: combine the two half-row sums, normalise once, store O and LSE.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -376,13 +418,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void fwd_pp_kernel(FwdPar
   }
 }
 
-template <int D, int BN, bool CAUSAL, int QB = 1, bool HP = false, int NW = 8>
+template <int D, int BN, bool CAUSAL, int QB = 1, bool HP = false, int NW = 8, int KS = 1>
 hipError_t run_pp(FwdParams p, long long B, hipStream_t st) {
   constexpr int BM = (HP ? 32 : 32 * QB) * NW;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * (HP ? p.Hq / 2 : p.Hq) * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL, QB, HP, NW>), dim3((int)nb), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((fwd_pp_kernel<D, BN, CAUSAL, QB, HP, NW, KS>), dim3((int)nb), dim3(64 * NW * KS),
+                     0, st, p);
   return hipGetLastError();
 }
 
