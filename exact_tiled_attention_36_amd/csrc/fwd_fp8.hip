@@ -431,10 +431,12 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_fp8_kernel(Fp8Params p) {
   }
 }
 
-// 8 waves (two per SIMD) up to d = 128; d = 256 needs one wave per SIMD for its registers
-template <int D, bool CAUSAL>
+// 8 waves (two per SIMD) up to d = 128; d = 256 needs one wave per SIMD for its registers.
+// Grids too small to give every compute unit a 256-row workgroup take 4-wave (128-row)
+// workgroups at d <= 128 too (NW4).
+template <int D, bool CAUSAL, bool NW4 = false>
 hipError_t run_fp8(Fp8Params p, long long B, hipStream_t st) {
-  constexpr int NW = D == 256 ? 4 : 8, BM = 32 * NW;
+  constexpr int NW = (D == 256 || NW4) ? 4 : 8, BM = 32 * NW;
   p.nqb = (p.Nq + BM - 1) / BM;
   const long long nb = (long long)p.nqb * p.Hq * B;
   if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -454,9 +456,14 @@ hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, 
   p.c2 = s.scale * descale_q * descale_k * kLog2e;
   p.descale_v = descale_v;
   const bool c = s.causal != 0;
+  const bool small = (long long)((s.Nq + 255) / 256) * s.Hq * s.B < 256;
   switch (s.d) {
-    case 64: return c ? run_fp8<64, true>(p, s.B, st) : run_fp8<64, false>(p, s.B, st);
-    case 128: return c ? run_fp8<128, true>(p, s.B, st) : run_fp8<128, false>(p, s.B, st);
+    case 64:
+      if (small) return c ? run_fp8<64, true, true>(p, s.B, st) : run_fp8<64, false, true>(p, s.B, st);
+      return c ? run_fp8<64, true>(p, s.B, st) : run_fp8<64, false>(p, s.B, st);
+    case 128:
+      if (small) return c ? run_fp8<128, true, true>(p, s.B, st) : run_fp8<128, false, true>(p, s.B, st);
+      return c ? run_fp8<128, true>(p, s.B, st) : run_fp8<128, false>(p, s.B, st);
     case 256: return c ? run_fp8<256, true>(p, s.B, st) : run_fp8<256, false>(p, s.B, st);
     default: return hipErrorInvalidValue;
   }
